@@ -1,0 +1,28 @@
+"""Compile the CPU oracle (plain C, double precision) into oracle/liboracle.so.
+
+Test infrastructure: the oracle is what the GPU library is checked against.
+Built with gcc -O2 (no fast-math, so every sum is evaluated as written) and
+OpenMP over the outer (batch, query) loops.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "sa_oracle.c")
+OUT = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter",
+           SRC, "-o", OUT + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
