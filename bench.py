@@ -1,0 +1,197 @@
+"""Benchmark of the DSA-style sparse-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: lightning indexer ->
+top-k -> sparse MLA, through the fused sparse_attn_decode C entry point, on
+seeded synthetic inputs already resident in HBM.
+
+Default workload: batched decode, B = 32 sequences x 1 query, L = 32768 cached
+tokens, indexer 64 heads x 128 (bf16), top-k 2048, MLA 128 heads, latent 512 +
+RoPE 64 (bf16), 16 planted needle rows per sequence.  Metric: decode
+queries/s; the whole step is also reported as a fraction of the HBM roofline
+(algorithmic bytes per query / step time / 8 TB/s).
+
+The JSON line carries, besides the contract fields:
+  roofline      the dominant kernel (the indexer) timed live with HIP events on
+                its own stream: algorithmic bytes per launch / mean duration,
+                against MI355X's 8 TB/s; `traffic` comes from rocprofv3
+                FETCH_SIZE/WRITE_SIZE counters or is null;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline] [--kernel-only]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_query(wl):
+    """Bytes one decode query must move at least once: indexer keys (+ fp8
+    scales), indexer query and weights, the gathered latent rows, the MLA
+    query and the fp32 output."""
+    kb = 1 if wl.k_idx.dtype.itemsize == 1 else wl.k_idx.element_size()
+    ki = wl.L * wl.dI * kb + (wl.L * 4 if wl.k_scale is not None else 0)
+    qi = wl.HI * wl.dI * wl.q_idx.element_size() + wl.HI * 4
+    gather = wl.topk * (wl.dc + wl.dR) * wl.kv.element_size()
+    qm = wl.H * (wl.dc + wl.dR) * wl.q_lat.element_size()
+    out = wl.H * wl.dc * 4
+    return ki, qi, gather, qm, out
+
+
+def make_workload(name):
+    from top_indexer_sparse_amd import workloads
+    if name == "decode_32k":
+        return workloads.decode_32k()
+    if name == "decode_128k_fp8":
+        return workloads.decode_128k_fp8()
+    raise SystemExit(f"unknown decode workload {name}")
+
+
+def time_events(fn, iters, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters  # ms
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """The oracle (unchanged) on a bounded sample of the workload: whole
+    sequences of the same batch, timed end to end (decode of the stored bytes,
+    indexer, top-k, sparse MLA)."""
+    import oracle
+    threads = oracle.num_threads()
+    n = max(1, min(wl.B, threads))
+    sub = wl.slice_batch(0, n)
+    t0 = time.perf_counter()
+    s = oracle.indexer(sub.q_idx, sub.w, sub.k_idx, k_scale=sub.k_scale, kv_len=sub.kv_len)
+    idx, _ = oracle.topk(s, sub.topk, kv_len=sub.kv_len)
+    oracle.sparse_mla(sub.q_lat, sub.q_rope, sub.kv, idx, sub.sm_scale, dc=sub.dc)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.B} sequences of {wl.name} (full L={wl.L}, k={wl.topk}, "
+                      f"H={wl.H}), fp64 C oracle with OpenMP over (query, head), "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only the fused steps (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from top_indexer_sparse_amd import api
+    api.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"generating {args.workload}")
+    wl = make_workload(args.workload)
+    t = wl.to(dev)
+    B, L, k = wl.B, wl.L, wl.topk
+    c_kv, k_rope = t.kv[..., :wl.dc], t.kv[..., wl.dc:]
+    out = torch.empty((B, 1, wl.H, wl.dc), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, 1, wl.H), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    nws = api.sparse_attn_workspace_bytes(api.SA_OP_DECODE, B, 1, L, k, wl.H, wl.dc)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.sparse_attn_decode(t.q_idx, t.w, t.k_idx, t.k_scale, t.kv_len, k, t.q_lat,
+                               t.q_rope, c_kv, k_rope, wl.sm_scale, out=out, lse=lse,
+                               idx_out=idx, ws=ws, stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    ms = time_events(step, args.steps, stream)
+    wall = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    qps = B / (ms * 1e-3)
+    ki, qi, gather, qm, o = algorithmic_bytes_per_query(wl)
+    per_q = ki + qi + gather + qm + o
+    step_frac = per_q * qps / (HBM_PEAK_GBS * 1e9)
+    log(f"{ms * 1e3:.1f} us/step, {qps:,.0f} queries/s, whole step {100 * step_frac:.1f}% "
+        f"of HBM peak ({wall:.2f} s wall)")
+    if args.kernel_only:
+        return
+
+    # dominant kernel: the indexer, timed alone on the same stream
+    scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
+
+    def idx_only():
+        api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, k_scale=t.k_scale,
+                                       kv_len=t.kv_len, scores=scores, stream=stream)
+
+    for _ in range(3):
+        idx_only()
+    idx_ms = time_events(idx_only, args.steps, stream)
+    idx_bytes = B * (ki + qi)
+    idx_gbs = idx_bytes / (idx_ms * 1e-3) / 1e9
+    log(f"indexer {idx_ms * 1e3:.1f} us/launch, {idx_gbs:,.0f} GB/s algorithmic")
+
+    result = {
+        "metric": "decode queries/s at L=32K,k=2048; indexer+gather % of HBM roofline",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.k_idx.dtype == torch.bfloat16 else "bf16+fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "L": L, "topk": k, "HI": wl.HI, "dI": wl.dI,
+                   "H": wl.H, "dc": wl.dc, "dR": wl.dR,
+                   "indexer_keys": str(wl.k_idx.dtype).replace("torch.", "")},
+        "hbm_frac_step": round(step_frac, 4),
+        "bytes_per_query": per_q,
+        "roofline": {"bound": "hbm", "kernel": "indexer", "achieved": round(idx_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us": round(idx_ms * 1e3, 2),
+                     "bytes_per_launch": idx_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

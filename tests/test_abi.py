@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sparse_attn.h, and rejects bad arguments on the host before
+anything is enqueued (validation runs before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from top_indexer_sparse_amd import api
+    return api.load()
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ("sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
+              "sparse_attn_decode", "sparse_attn_workspace_bytes", "sparse_attn_status_string",
+              "sparse_attn_last_error", "sparse_attn_block_pool", "sparse_attn_block_decode"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from top_indexer_sparse_amd import api
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sparse_attn_\w+)", out))
+    for n in declared():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    assert set(api.EXPORTS) == set(declared())
+
+
+def test_library_carries_gfx950_code_objects():
+    from top_indexer_sparse_amd import api
+    blob = open(api.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def _err(lib):
+    return lib.sparse_attn_last_error().decode()
+
+
+def test_status_strings(lib):
+    assert lib.sparse_attn_status_string(0) == b"SA_OK"
+    assert lib.sparse_attn_status_string(7) == b"SA_ERR_HIP"
+    assert lib.sparse_attn_status_string(99) == b"SA_UNKNOWN_STATUS"
+
+
+P = ctypes.c_void_p
+A = P(0x10000)  # aligned dummy device address; never dereferenced by validation
+M = P(0x10004)  # misaligned
+
+
+def test_indexer_validation(lib):
+    f = lib.sparse_attn_indexer_scores
+    # NULL required pointer
+    assert f(None, 1, A, A, 1, None, None, None, 1, 1, 8, 64, 128, A, None) == 1
+    # bad dtype
+    assert f(A, 5, A, A, 1, None, None, None, 1, 1, 8, 64, 128, A, None) == 3
+    # fp8 keys without scales
+    assert f(A, 1, A, A, 2, None, None, None, 1, 1, 8, 64, 128, A, None) == 1
+    # unsupported dI
+    assert f(A, 1, A, A, 1, None, None, None, 1, 1, 8, 64, 96, A, None) == 5
+    assert "dI=96" in _err(lib)
+    # misaligned
+    assert f(M, 1, A, A, 1, None, None, None, 1, 1, 8, 64, 128, A, None) == 4
+    # negative size
+    assert f(A, 1, A, A, 1, None, None, None, -1, 1, 8, 64, 128, A, None) == 2
+
+
+def test_topk_validation(lib):
+    f = lib.sparse_attn_topk
+    assert f(None, None, None, 1, 1, 8, 4, A, None, None, 0, None) == 1
+    assert f(A, None, None, 1, 1, 8, 0, A, None, None, 0, None) == 2
+    assert f(A, None, None, 1, 1, 8, 5000, A, None, None, 0, None) == 5
+    # a long row needs a workspace
+    assert f(A, None, None, 1, 1, 100000, 2048, A, None, None, 0, None) == 6
+    assert lib.sparse_attn_workspace_bytes(0, 1, 1, 100000, 2048, 0, 0) > 0
+    assert lib.sparse_attn_workspace_bytes(0, 1, 1, 32768, 2048, 0, 0) == 0
+
+
+def test_mla_validation(lib):
+    f = lib.sparse_attn_mla_forward
+    F = ctypes.c_float(0.1)
+    # dtype mismatch
+    assert f(A, A, 1, A, A, 0, 576, 576, A, 64, 1, 1, 10, 128, 512, 64, F, A, None, None, 0, None) == 3
+    # unsupported shape on the bf16 path (H not a multiple of 64 and too big for the vector path)
+    assert f(A, A, 1, A, A, 1, 576, 576, A, 64, 1, 1, 10, 100, 512, 64, F, A, None, None, 0, None) == 5
+    # stride shorter than the row
+    assert f(A, A, 1, A, A, 1, 500, 576, A, 64, 1, 1, 10, 128, 512, 64, F, A, None, None, 0, None) == 2
+    # row stride breaking alignment (fp32, 161 elements)
+    assert f(A, A, 0, A, A, 0, 161, 161, A, 64, 1, 1, 10, 8, 128, 32, F, A, None, None, 0, None) == 4
+    # missing workspace for a KV split (B=1, k=2048 splits over work-groups)
+    assert lib.sparse_attn_workspace_bytes(1, 1, 1, 32768, 2048, 128, 512) > 0
+    assert f(A, A, 1, A, A, 1, 576, 576, A, 2048, 1, 1, 32768, 128, 512, 64, F, A, None, None, 0, None) == 6
+
+
+def test_decode_validation(lib):
+    f = lib.sparse_attn_decode
+    F = ctypes.c_float(0.1)
+    args = [A, 1, A, A, 1, None, None, 2, 4096, 64, 128, 2048, A, A, 1, A, A, 1, 576, 576, 128,
+            512, 64, F, A, None, None]
+    assert f(*args, None, 0, None) == 6
+    need = lib.sparse_attn_workspace_bytes(2, 2, 1, 4096, 2048, 128, 512)
+    assert need >= 2 * 4096 * 4
+    assert f(*args, A, need - 256, None) == 6

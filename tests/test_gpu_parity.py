@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes the oracle finishes in seconds, spanning several tiles and a ragged
+tail, plus edge cases (ragged kv_len, empty rows, k above the candidate
+count, ties).  Full-size workloads are in test_gpu_fullsize.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_indexer_sparse_amd import api, workloads
+from parity import (ATTN_ATOL_BF16, assert_attention_close, assert_index_sets,
+                    assert_scores_close, score_floor)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _cuda(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# --------------------------------------------------------------------------
+# indexer
+# --------------------------------------------------------------------------
+
+def test_indexer_exact_small_integers():
+    wl = workloads.tiny_prefill()
+    _announce("indexer tiny_prefill fp32 L=1024")
+    q, w, k, qp = _cuda(wl.q_idx, wl.w, wl.k_idx, wl.q_pos)
+    g = api.sparse_attn_indexer_scores(q, w, k, q_pos=qp)
+    torch.cuda.synchronize()
+    ref = oracle.indexer(wl.q_idx, wl.w, wl.k_idx, q_pos=wl.q_pos)
+    assert np.array_equal(g.cpu().double().numpy(), ref)  # bit-exact
+
+
+@pytest.mark.parametrize("HI,dI,fp8", [(64, 128, False), (16, 128, False), (32, 64, False),
+                                       (128, 128, False), (64, 128, True), (16, 64, True)])
+def test_indexer_mfma_decode(HI, dI, fp8):
+    _announce(f"indexer decode HI={HI} dI={dI} fp8={fp8}")
+    B, L = 3, 3001
+    kv_len = [3001, 1777, 5]
+    if fp8:
+        wl = workloads.decode_128k_fp8(B=B, L=L, HI=HI, dI=dI, H=64, boost_frac=0.02)
+        wl.kv_len = torch.tensor(kv_len, dtype=torch.int32)
+    else:
+        wl = workloads.decode_32k(B=B, L=L, HI=HI, dI=dI, H=64, kv_len=kv_len, n_needles=4)
+    q, w, k, ks, kl = _cuda(wl.q_idx, wl.w, wl.k_idx, wl.k_scale, wl.kv_len)
+    g = api.sparse_attn_indexer_scores(q, w, k, k_scale=ks, kv_len=kl)
+    torch.cuda.synchronize()
+    ref = oracle.indexer(wl.q_idx, wl.w, wl.k_idx, k_scale=wl.k_scale, kv_len=wl.kv_len)
+    fl = score_floor(wl.q_idx, wl.w, oracle.dequantized_keys(wl.k_idx, wl.k_scale))
+    assert_scores_close(g, ref, fl)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_indexer_mfma_prefill(fp8):
+    _announce(f"indexer prefill L=520 fp8={fp8}")
+    L = 520
+    wl = workloads.prefill_16k(L=L, with_mla=False, n_needles=0)
+    k_idx, k_scale = wl.k_idx, None
+    if fp8:
+        k32 = wl.k_idx.float()
+        k_scale = k32.abs().amax(-1) / 448.0
+        k_idx = (k32 / k_scale[..., None]).to(torch.float8_e4m3fn)
+    # a second sequence with a shorter cache exercises kv_len with q_pos
+    q_idx = torch.cat([wl.q_idx, wl.q_idx.flip(1)])
+    w = torch.cat([wl.w, wl.w.flip(1)])
+    k_idx = torch.cat([k_idx, k_idx.flip(1)])
+    k_scale = None if k_scale is None else torch.cat([k_scale, k_scale.flip(1)])
+    q_pos = torch.cat([wl.q_pos, wl.q_pos])
+    kv_len = torch.tensor([L, 301], dtype=torch.int32)
+    q, ww, k, ks, qp, kl = _cuda(q_idx, w, k_idx, k_scale, q_pos, kv_len)
+    g = api.sparse_attn_indexer_scores(q, ww, k, k_scale=ks, q_pos=qp, kv_len=kl)
+    torch.cuda.synchronize()
+    ref = oracle.indexer(q_idx, w, k_idx, k_scale=k_scale, q_pos=q_pos, kv_len=kv_len)
+    fl = score_floor(q_idx, w, oracle.dequantized_keys(k_idx, k_scale))
+    assert_scores_close(g, ref, fl)
+
+
+def test_indexer_vector_path_bf16_odd_heads():
+    _announce("indexer vector path HI=12 bf16")
+    g0 = torch.Generator().manual_seed(5)
+    B, T, HI, dI, L = 2, 3, 12, 64, 257
+    q = torch.randn(B, T, HI, dI, generator=g0).to(torch.bfloat16)
+    w = torch.rand(B, T, HI, generator=g0) - 0.3  # negative weights are allowed
+    k = torch.randn(B, L, dI, generator=g0).to(torch.bfloat16)
+    qp = torch.tensor([[0, 100, 256], [5, 6, 300]], dtype=torch.int32)
+    gq, gw, gk, gqp = _cuda(q, w, k, qp)
+    g = api.sparse_attn_indexer_scores(gq, gw, gk, q_pos=gqp)
+    torch.cuda.synchronize()
+    ref = oracle.indexer(q, w, k, q_pos=qp)
+    assert_scores_close(g, ref, score_floor(q, w, oracle.decode(k)))
+
+
+# --------------------------------------------------------------------------
+# top-k (same scores on both sides -> identical sets)
+# --------------------------------------------------------------------------
+
+def _topk_both(scores, k, q_pos=None, kv_len=None):
+    gi, gc = api.sparse_attn_topk(*_cuda(scores), k, *_cuda(q_pos, kv_len))
+    torch.cuda.synchronize()
+    oi, oc = oracle.topk(scores.double().numpy(), k, q_pos=q_pos, kv_len=kv_len)
+    return gi.cpu().numpy(), gc.cpu().numpy(), oi, oc
+
+
+def test_topk_exact_small_integer_workload():
+    _announce("topk tiny_prefill k=64 (many ties)")
+    wl = workloads.tiny_prefill()
+    s = torch.from_numpy(oracle.indexer(wl.q_idx, wl.w, wl.k_idx, q_pos=wl.q_pos)).float()
+    gi, gc, oi, oc = _topk_both(s, 64, q_pos=wl.q_pos)
+    assert np.array_equal(gc, oc) and np.array_equal(gi, oi)
+
+
+@pytest.mark.parametrize("L,k,kind", [(5000, 2048, "normal"), (32768, 2048, "ties"),
+                                      (32768, 4096, "signed"), (1000, 1, "ties"),
+                                      (70000, 2048, "ties"), (131072, 2048, "normal"),
+                                      (40000, 64, "zeros")])
+def test_topk_matches_oracle_bitexact(L, k, kind):
+    _announce(f"topk L={L} k={k} {kind}")
+    g0 = torch.Generator().manual_seed(L + k)
+    B = 3
+    if kind == "normal":
+        s = torch.randn(B, 1, L, generator=g0).abs()
+    elif kind == "ties":
+        s = torch.randint(0, 40, (B, 1, L), generator=g0).float() * 0.25
+    elif kind == "zeros":
+        s = torch.zeros(B, 1, L)
+        s[:, :, ::97] = 1.0
+        s[:, :, 1::5] = -0.0
+    else:
+        s = torch.randn(B, 1, L, generator=g0) * 1e3
+        s[:, :, ::7] = -s[:, :, ::7].abs()
+    kv_len = torch.tensor([L, L // 2 + 3, min(k, L) - 1 if min(k, L) > 1 else 1],
+                          dtype=torch.int32)
+    gi, gc, oi, oc = _topk_both(s, k, kv_len=kv_len)
+    assert np.array_equal(gc, oc)
+    assert np.array_equal(gi, oi)
+
+
+def test_topk_causal_rows_and_empty():
+    _announce("topk causal rows, empty rows")
+    g0 = torch.Generator().manual_seed(9)
+    T, L, k = 70, 200, 16
+    s = torch.randn(2, T, L, generator=g0)
+    q_pos = torch.arange(T, dtype=torch.int32).repeat(2, 1)
+    q_pos[1, :5] = -1  # queries with no candidate
+    kv_len = torch.tensor([L, 0], dtype=torch.int32)
+    gi, gc, oi, oc = _topk_both(s, k, q_pos=q_pos, kv_len=kv_len)
+    assert np.array_equal(gc, oc) and np.array_equal(gi, oi)
+    assert np.all(gc[1] == 0) and np.all(gi[1] == -1)
+
+
+def test_topk_excludes_nan_and_neg_inf():
+    # documented GPU behaviour: NaN and -inf scores are never selected
+    _announce("topk NaN/-inf exclusion")
+    s = torch.tensor([[[1.0, float("nan"), 3.0, float("-inf"), 2.0, float("inf")]]])
+    gi, gc = api.sparse_attn_topk(s.to(DEV), 4)
+    torch.cuda.synchronize()
+    assert gc.item() == 4
+    assert gi.cpu().tolist() == [[[0, 2, 4, 5]]]
+
+
+# --------------------------------------------------------------------------
+# sparse MLA given identical indices
+# --------------------------------------------------------------------------
+
+def test_mla_fp32_vector_path():
+    _announce("mla fp32 tiny_prefill dims")
+    wl = workloads.tiny_prefill(L=300, topk=64)
+    s = oracle.indexer(wl.q_idx, wl.w, wl.k_idx, q_pos=wl.q_pos)
+    oi, oc = oracle.topk(s, wl.topk, q_pos=wl.q_pos)
+    ql, qr, kv, idx = _cuda(wl.q_lat, wl.q_rope, wl.kv, torch.from_numpy(oi))
+    out, lse = api.sparse_attn_mla_forward(ql, qr, kv[..., :wl.dc], kv[..., wl.dc:], idx,
+                                           wl.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, oi, wl.sm_scale, dc=wl.dc)
+    err = assert_attention_close(out, ro, 2e-3, lse, rl)
+    assert err < 1e-4  # fp32 arithmetic
+
+
+@pytest.mark.parametrize("B,k,H", [(2, 2048, 128), (5, 300, 64), (40, 96, 128)])
+def test_mla_bf16_mfma(B, k, H):
+    _announce(f"mla bf16 B={B} k={k} H={H}")
+    L = 2600
+    wl = workloads.decode_32k(B=B, L=L, H=H, n_needles=16 if B < 10 else 0)
+    rng = np.random.default_rng(B * 1000 + k)
+    idx = np.stack([np.sort(rng.choice(L, k, replace=False)) for _ in range(B)])[:, None]
+    idx = idx.astype(np.int32)
+    if wl.needles is not None:  # put the needles in the set (duplicates count twice)
+        for b in range(B):
+            idx[b, 0, :16] = wl.needles[b].numpy()
+    idx[0, 0, -7:] = -1          # padding slots are skipped
+    idx[-1, 0, 3] = L + 5        # out-of-range slot is skipped
+    ql, qr, kv, gidx = _cuda(wl.q_lat, wl.q_rope, wl.kv, torch.from_numpy(idx))
+    out, lse = api.sparse_attn_mla_forward(ql, qr, kv[..., :wl.dc], kv[..., wl.dc:], gidx,
+                                           wl.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, idx, wl.sm_scale, dc=wl.dc)
+    assert_attention_close(out, ro, ATTN_ATOL_BF16, lse, rl)
+
+
+def test_mla_empty_rows_give_zero_and_neg_inf():
+    _announce("mla empty rows")
+    wl = workloads.decode_32k(B=2, L=300, H=64, n_needles=0)
+    idx = np.full((2, 1, 64), -1, dtype=np.int32)
+    idx[1, 0, :10] = np.arange(10)
+    ql, qr, kv, gidx = _cuda(wl.q_lat, wl.q_rope, wl.kv, torch.from_numpy(idx))
+    out, lse = api.sparse_attn_mla_forward(ql, qr, kv[..., :wl.dc], kv[..., wl.dc:], gidx,
+                                           wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    ro, rl = oracle.sparse_mla(wl.q_lat[1:], wl.q_rope[1:], wl.kv[1:], idx[1:], wl.sm_scale,
+                               dc=wl.dc)
+    assert_attention_close(out[1:], ro, ATTN_ATOL_BF16, lse[1:], rl)
+
+
+def test_mla_separate_cache_tensors_fp32_rope_stride():
+    # c_kv and k_rope as two separate tensors (different row strides)
+    _announce("mla separate caches")
+    g0 = torch.Generator().manual_seed(3)
+    B, T, H, dc, dR, L, k = 2, 2, 8, 128, 32, 90, 40
+    ql = torch.randn(B, T, H, dc, generator=g0)
+    qr = torch.randn(B, T, H, dR, generator=g0)
+    c = torch.randn(B, L, dc, generator=g0)
+    r = torch.randn(B, L, dR, generator=g0)
+    idx = torch.stack([torch.stack([torch.randperm(L, generator=g0)[:k] for _ in range(T)])
+                       for _ in range(B)]).to(torch.int32)
+    out, lse = api.sparse_attn_mla_forward(*_cuda(ql, qr, c, r, idx), 0.1)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla(ql, qr, c, idx.numpy(), 0.1, dc=dc, k_rope=r)
+    assert_attention_close(out, ro, 1e-4, lse, rl)
+
+
+# --------------------------------------------------------------------------
+# fused decode and the whole path
+# --------------------------------------------------------------------------
+
+def test_fused_decode_small():
+    _announce("fused decode B=4 L=5000 k=2048")
+    B, L = 4, 5000
+    wl = workloads.decode_32k(B=B, L=L, kv_len=[5000, 4000, 2100, 1500])
+    t = wl.to(DEV)
+    out, lse, idx = api.sparse_attn_decode(t.q_idx, t.w, t.k_idx, None, t.kv_len, wl.topk,
+                                           t.q_lat, t.q_rope, t.kv[..., :wl.dc],
+                                           t.kv[..., wl.dc:], wl.sm_scale)
+    torch.cuda.synchronize()
+    s = oracle.indexer(wl.q_idx, wl.w, wl.k_idx, kv_len=wl.kv_len)
+    oi, oc = oracle.topk(s, wl.topk, kv_len=wl.kv_len)
+    gi = idx.cpu().numpy()
+    gc = (gi >= 0).sum(-1)
+    assert_index_sets(gi, gc, oi, oc, s)
+    # needles are found (sanity, not parity)
+    for b in range(B):
+        assert set(wl.needles[b].tolist()) <= set(gi[b, 0].tolist())
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, gi, wl.sm_scale, dc=wl.dc)
+    assert_attention_close(out, ro, ATTN_ATOL_BF16, lse, rl)
+
+
+def test_staged_path_equals_fused_decode():
+    _announce("staged == fused decode")
+    B, L = 3, 4100
+    wl = workloads.decode_32k(B=B, L=L)
+    t = wl.to(DEV)
+    s = api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx)
+    idx, cnt = api.sparse_attn_topk(s, wl.topk)
+    out, lse = api.sparse_attn_mla_forward(t.q_lat, t.q_rope, t.kv[..., :wl.dc],
+                                           t.kv[..., wl.dc:], idx, wl.sm_scale)
+    out2, lse2, idx2 = api.sparse_attn_decode(t.q_idx, t.w, t.k_idx, None, None, wl.topk,
+                                              t.q_lat, t.q_rope, t.kv[..., :wl.dc],
+                                              t.kv[..., wl.dc:], wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_prefill_path_small_causal():
+    _announce("prefill path L=200 H=64")
+    L = 200
+    wl = workloads.prefill_16k(L=L, H=64, topk=64)
+    t = wl.to(DEV)
+    s = api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, q_pos=t.q_pos)
+    idx, cnt = api.sparse_attn_topk(s, wl.topk, q_pos=t.q_pos)
+    out, lse = api.sparse_attn_mla_forward(t.q_lat, t.q_rope, t.kv[..., :wl.dc],
+                                           t.kv[..., wl.dc:], idx, wl.sm_scale)
+    torch.cuda.synchronize()
+    rs = oracle.indexer(wl.q_idx, wl.w, wl.k_idx, q_pos=wl.q_pos)
+    oi, oc = oracle.topk(rs, wl.topk, q_pos=wl.q_pos)
+    assert_index_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, rs)
+    gi = idx.cpu().numpy()
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, gi, wl.sm_scale, dc=wl.dc)
+    assert_attention_close(out, ro, ATTN_ATOL_BF16, lse, rl)
+    # causality: no selected position after its query
+    for t_ in range(L):
+        sel = gi[0, t_][gi[0, t_] >= 0]
+        assert sel.max() <= t_

@@ -1,0 +1,254 @@
+// api.cpp -- the extern "C" entry points of libsparse_attn.so.
+//
+// Each entry point validates every argument on the host, then enqueues the
+// kernels on the caller's stream.  Nothing is allocated and nothing waits.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+#include "sparse_attn.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SA_OK;
+  return fail(SA_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+size_t dtype_size(int dt) { return dt == SA_F32 ? 4 : dt == SA_BF16 ? 2 : dt == SA_FP8_E4M3 ? 1 : 0; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+int check_indexer(const sa::IndexerArgs& a) {
+  REQUIRE(a.q && a.w && a.k && a.scores, SA_ERR_NULL, "indexer: q_idx, w, k_idx and scores are required");
+  REQUIRE(a.B >= 0 && a.T >= 0 && a.L >= 0, SA_ERR_SHAPE, "indexer: negative size B=%d T=%d L=%d", a.B, a.T, a.L);
+  REQUIRE(a.HI >= 1 && a.dI >= 1, SA_ERR_SHAPE, "indexer: HI=%d dI=%d must be >= 1", a.HI, a.dI);
+  REQUIRE(a.q_dtype == SA_F32 || a.q_dtype == SA_BF16, SA_ERR_DTYPE, "indexer: q_dtype %d not in {F32, BF16}", a.q_dtype);
+  REQUIRE(a.k_dtype == SA_F32 || a.k_dtype == SA_BF16 || a.k_dtype == SA_FP8_E4M3, SA_ERR_DTYPE,
+          "indexer: k_dtype %d not in {F32, BF16, FP8_E4M3}", a.k_dtype);
+  REQUIRE((a.k_dtype == SA_FP8_E4M3) == (a.k_scale != nullptr), SA_ERR_NULL,
+          "indexer: k_scale is required for fp8 keys and must be NULL otherwise");
+  REQUIRE(a.dI == 64 || a.dI == 128, SA_ERR_UNSUPPORTED, "indexer: dI=%d not in {64, 128}", a.dI);
+  REQUIRE(a.HI <= 128, SA_ERR_UNSUPPORTED, "indexer: HI=%d > 128", a.HI);
+  REQUIRE(sa::indexer_uses_mfma(a) || a.HI <= 64, SA_ERR_UNSUPPORTED,
+          "indexer: HI=%d > 64 needs the bf16 MFMA path (bf16 q, bf16/fp8 k, HI in {16,32,64,128})", a.HI);
+  REQUIRE(aligned16(a.q) && aligned16(a.w) && aligned16(a.k) && aligned16(a.scores) &&
+              aligned16(a.k_scale) && aligned16(a.q_pos) && aligned16(a.kv_len),
+          SA_ERR_ALIGN, "indexer: every pointer must be 16-byte aligned");
+  return SA_OK;
+}
+
+int check_topk(const sa::TopkArgs& a, size_t ws_bytes) {
+  REQUIRE(a.scores && a.idx, SA_ERR_NULL, "topk: scores and idx are required");
+  REQUIRE(a.B >= 0 && a.T >= 0 && a.L >= 0, SA_ERR_SHAPE, "topk: negative size B=%d T=%d L=%d", a.B, a.T, a.L);
+  REQUIRE(a.k >= 1, SA_ERR_SHAPE, "topk: k=%d must be >= 1", a.k);
+  REQUIRE(sa::topk_supported(a.L, a.k), SA_ERR_UNSUPPORTED,
+          "topk: k=%d, L=%d outside the compiled set (k <= %d, ceil(L/32768)*k <= 32768)", a.k, a.L,
+          sa::kTopkMaxK);
+  REQUIRE(aligned16(a.scores) && aligned16(a.idx) && aligned16(a.count) && aligned16(a.q_pos) &&
+              aligned16(a.kv_len) && aligned16(a.ws),
+          SA_ERR_ALIGN, "topk: every pointer must be 16-byte aligned");
+  const size_t need = sa::topk_workspace_bytes(a.B, a.T, a.L, a.k);
+  REQUIRE(need == 0 || (a.ws && ws_bytes >= need), SA_ERR_WORKSPACE,
+          "topk: workspace of %zu bytes required, %zu given", need, a.ws ? ws_bytes : (size_t)0);
+  return SA_OK;
+}
+
+int check_mla(const sa::MlaArgs& a, size_t ws_bytes) {
+  REQUIRE(a.q_lat && a.c_kv && a.idx && a.out, SA_ERR_NULL, "mla: q_lat, c_kv, idx and out are required");
+  REQUIRE(a.dR == 0 || (a.q_rope && a.k_rope), SA_ERR_NULL, "mla: q_rope and k_rope are required when dR > 0");
+  REQUIRE(a.B >= 0 && a.T >= 0 && a.L >= 1 && a.k >= 1 && a.H >= 1 && a.dc >= 1 && a.dR >= 0, SA_ERR_SHAPE,
+          "mla: bad size B=%d T=%d L=%d k=%d H=%d dc=%d dR=%d", a.B, a.T, a.L, a.k, a.H, a.dc, a.dR);
+  REQUIRE(a.dtype == SA_F32 || a.dtype == SA_BF16, SA_ERR_DTYPE, "mla: dtype %d not in {F32, BF16}", a.dtype);
+  REQUIRE(a.c_stride >= a.dc && (a.dR == 0 || a.r_stride >= a.dR), SA_ERR_SHAPE,
+          "mla: row strides (%lld, %lld) shorter than the rows (%d, %d)", (long long)a.c_stride,
+          (long long)a.r_stride, a.dc, a.dR);
+  REQUIRE(sa::mla_supported(a), SA_ERR_UNSUPPORTED,
+          "mla: (dtype=%d, H=%d, dc=%d, dR=%d) outside the compiled set", a.dtype, a.H, a.dc, a.dR);
+  const size_t es = dtype_size(a.dtype);
+  REQUIRE(aligned16(a.q_lat) && aligned16(a.q_rope) && aligned16(a.c_kv) && aligned16(a.k_rope) &&
+              aligned16(a.idx) && aligned16(a.out) && aligned16(a.lse) && aligned16(a.ws) &&
+              (a.c_stride * es) % 16 == 0 && (a.dR == 0 || (a.r_stride * es) % 16 == 0),
+          SA_ERR_ALIGN, "mla: pointers and row strides must keep 16-byte alignment");
+  const size_t need = sa::mla_workspace_bytes(a.dtype, a.B, a.T, a.k, a.H, a.dc);
+  REQUIRE(need == 0 || (a.ws && ws_bytes >= need), SA_ERR_WORKSPACE,
+          "mla: workspace of %zu bytes required, %zu given", need, a.ws ? ws_bytes : (size_t)0);
+  return SA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// decode workspace layout: scores [B, L] f32 | idx [B, k] | count [B] | topk ws | mla ws
+struct DecodeWs {
+  size_t scores, idx, count, topk, mla, total;
+};
+DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype) {
+  DecodeWs w{};
+  size_t off = 0;
+  w.scores = off;
+  off = align256(off + (size_t)B * L * sizeof(float));
+  w.idx = off;
+  off = align256(off + (size_t)B * k * sizeof(int32_t));
+  w.count = off;
+  off = align256(off + (size_t)B * sizeof(int32_t));
+  w.topk = off;
+  off = align256(off + sa::topk_workspace_bytes(B, 1, L, k));
+  w.mla = off;
+  off = align256(off + sa::mla_workspace_bytes(kv_dtype, B, 1, k, H, dc));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_indexer_scores(const void* q_idx, int q_dtype, const float* w, const void* k_idx,
+                               int k_dtype, const float* k_scale, const int32_t* q_pos,
+                               const int32_t* kv_len, int B, int T, int L, int HI, int dI,
+                               float* scores, void* stream) {
+  clear_error();
+  sa::IndexerArgs a{q_idx, q_dtype, w, k_idx, k_dtype, k_scale, q_pos, kv_len, B, T, L, HI, dI, scores};
+  int s = check_indexer(a);
+  if (s != SA_OK) return s;
+  return hip_status(sa::launch_indexer(a, (hipStream_t)stream), "indexer launch");
+}
+
+int sparse_attn_topk(const float* scores, const int32_t* q_pos, const int32_t* kv_len, int B, int T,
+                     int L, int k, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                     void* stream) {
+  clear_error();
+  sa::TopkArgs a{scores, q_pos, kv_len, B, T, L, k, idx, count, ws};
+  int s = check_topk(a, ws_bytes);
+  if (s != SA_OK) return s;
+  return hip_status(sa::launch_topk(a, (hipStream_t)stream), "topk launch");
+}
+
+int sparse_attn_mla_forward(const void* q_lat, const void* q_rope, int q_dtype, const void* c_kv,
+                            const void* k_rope, int kv_dtype, int64_t c_stride, int64_t r_stride,
+                            const int32_t* idx, int k, int B, int T, int L, int H, int dc, int dR,
+                            float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+  clear_error();
+  if (q_dtype != kv_dtype) return fail(SA_ERR_DTYPE, "mla: q_dtype %d != kv_dtype %d", q_dtype, kv_dtype);
+  sa::MlaArgs a{q_lat, q_rope, q_dtype, c_kv, k_rope, c_stride, r_stride, idx, k, B, T, L, H, dc, dR,
+                sm_scale, out, lse, ws};
+  int s = check_mla(a, ws_bytes);
+  if (s != SA_OK) return s;
+  return hip_status(sa::launch_mla(a, (hipStream_t)stream), "mla launch");
+}
+
+int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w, const void* k_idx,
+                       int k_dtype, const float* k_scale, const int32_t* kv_len, int B, int L,
+                       int HI, int dI, int k, const void* q_lat, const void* q_rope, int q_dtype,
+                       const void* c_kv, const void* k_rope, int kv_dtype, int64_t c_stride,
+                       int64_t r_stride, int H, int dc, int dR, float sm_scale, float* out,
+                       float* lse, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (q_dtype != kv_dtype) return fail(SA_ERR_DTYPE, "decode: q_dtype %d != kv_dtype %d", q_dtype, kv_dtype);
+  if (!ws) return fail(SA_ERR_WORKSPACE, "decode: a workspace is required");
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "decode: workspace must be 16-byte aligned");
+  const DecodeWs lay = decode_ws(B < 0 ? 0 : B, L < 0 ? 0 : L, k < 1 ? 1 : k, H, dc, kv_dtype);
+  char* base = (char*)ws;
+  float* scores = (float*)(base + lay.scores);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + lay.idx);
+  int32_t* count = (int32_t*)(base + lay.count);
+  sa::IndexerArgs ia{q_idx, q_idx_dtype, w, k_idx, k_dtype, k_scale, nullptr, kv_len, B, 1, L, HI, dI, scores};
+  sa::TopkArgs ta{scores, nullptr, kv_len, B, 1, L, k, idx, count, base + lay.topk};
+  sa::MlaArgs ma{q_lat, q_rope, q_dtype, c_kv, k_rope, c_stride, r_stride, idx, k, B, 1, L, H, dc, dR,
+                 sm_scale, out, lse, base + lay.mla};
+  int s = check_indexer(ia);
+  if (s == SA_OK) s = check_topk(ta, lay.mla - lay.topk);
+  if (s == SA_OK) s = check_mla(ma, lay.total - lay.mla);
+  if (s == SA_OK && ws_bytes < lay.total)
+    s = fail(SA_ERR_WORKSPACE, "decode: workspace of %zu bytes required, %zu given", lay.total, ws_bytes);
+  if (s != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  s = hip_status(sa::launch_indexer(ia, st), "decode indexer launch");
+  if (s == SA_OK) s = hip_status(sa::launch_topk(ta, st), "decode topk launch");
+  if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "decode mla launch");
+  return s;
+}
+
+int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, float* krep,
+                           void* stream) {
+  clear_error();
+  REQUIRE(k && krep, SA_ERR_NULL, "block_pool: k and krep are required");
+  REQUIRE(B >= 0 && L >= 0 && Hkv >= 1 && blk >= 1, SA_ERR_SHAPE, "block_pool: bad size");
+  REQUIRE(d == 128, SA_ERR_UNSUPPORTED, "block_pool: d=%d not 128", d);
+  REQUIRE(blk == 32 || blk == 64 || blk == 128, SA_ERR_UNSUPPORTED, "block_pool: blk=%d not in {32,64,128}", blk);
+  REQUIRE(aligned16(k) && aligned16(krep), SA_ERR_ALIGN, "block_pool: pointers must be 16-byte aligned");
+  return hip_status(sa::launch_block_pool(k, B, L, Hkv, d, blk, krep, (hipStream_t)stream), "block_pool launch");
+}
+
+int sparse_attn_block_decode(const void* q, const void* k, const void* v, const float* krep, int B,
+                             int L, int Hq, int Hkv, int d, int blk, int nsel, int n_sink,
+                             int n_win, float sm_scale, float* out, int32_t* blocks_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  clear_error();
+  sa::BlockArgs a{q, k, v, krep, B, L, Hq, Hkv, d, blk, nsel, n_sink, n_win, sm_scale, out, blocks_out, ws};
+  REQUIRE(q && k && v && krep && out, SA_ERR_NULL, "block_decode: q, k, v, krep and out are required");
+  REQUIRE(B >= 0 && L >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && n_sink >= 0 && n_win >= 0 && nsel >= 1,
+          SA_ERR_SHAPE, "block_decode: bad size");
+  REQUIRE(sa::block_supported(a), SA_ERR_UNSUPPORTED, "block_decode: dims outside the compiled set");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(krep) && aligned16(out) &&
+              aligned16(blocks_out) && aligned16(ws),
+          SA_ERR_ALIGN, "block_decode: pointers must be 16-byte aligned");
+  const size_t need = sa::block_workspace_bytes(B, Hq, L, nsel, Hkv, d, blk);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need), SA_ERR_WORKSPACE,
+          "block_decode: workspace of %zu bytes required, %zu given", need, ws ? ws_bytes : (size_t)0);
+  return hip_status(sa::launch_block_decode(a, (hipStream_t)stream), "block_decode launch");
+}
+
+size_t sparse_attn_workspace_bytes(int op, int B, int T, int L, int k, int H, int dc) {
+  if (B < 0 || T < 0 || L < 0 || k < 1) return 0;
+  switch (op) {
+    case SA_OP_TOPK:
+      return sa::topk_workspace_bytes(B, T, L, k);
+    case SA_OP_MLA_FORWARD:
+      return sa::mla_workspace_bytes(SA_BF16, B, T, k, H, dc);
+    case SA_OP_DECODE:
+      return decode_ws(B, L, k, H, dc, SA_BF16).total;
+    case SA_OP_BLOCK_DECODE:  // (B, Hq, L, nsel, Hkv, d) passed as (B, T, L, k, H, dc)
+      return sa::block_workspace_bytes(B, T, L, k, H, dc, 64);
+  }
+  return 0;
+}
+
+const char* sparse_attn_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL: return "SA_ERR_NULL";
+    case SA_ERR_SHAPE: return "SA_ERR_SHAPE";
+    case SA_ERR_DTYPE: return "SA_ERR_DTYPE";
+    case SA_ERR_ALIGN: return "SA_ERR_ALIGN";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+  }
+  return "SA_UNKNOWN_STATUS";
+}
+
+const char* sparse_attn_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libsparse_attn.
+//
+// Lane layouts of the bf16 MFMA instructions used here (checked on gfx950):
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     lane l supplies A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e < 8,
+//     and holds D[4*(l/16) + r][l%16], r < 4.
+// The contraction index may be permuted freely as long as A and B use the same
+// permutation; the kernels rely on that to load 16-byte runs.
+//
+// ds_read_b64_tr_b16 (gfx950 LDS transpose read): inside each group of 16
+// lanes, lane i receives as element r the 16-bit value at position i%4 of the
+// 8-byte chunk addressed by lane 4*r + i/4 of the same group.  Pointing lane
+// 4*r + q at row (R0 + r), columns (C0 + 4q .. C0 + 4q + 3) of a row-major
+// bf16 tile therefore gives lane i the column C0 + i of rows R0 .. R0 + 3: the
+// operand layout of a product contracted over rows.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
+  return __builtin_bit_cast(float, b16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t packed) {
+  return __builtin_bit_cast(float, packed << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {
+  return __builtin_bit_cast(float, packed & 0xffff0000u);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t float_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  return float_to_bf16_rne(lo) | (float_to_bf16_rne(hi) << 16);
+}
+// Exact packing of two fp32 values that are representable in bf16.
+__device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi),
+                               __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// Four OCP e4m3fn codes (one dword) -> four bf16 values (two dwords), exact:
+// every e4m3fn value, subnormals included, is representable in bf16.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t codes, uint32_t& out01,
+                                                uint32_t& out23) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+  out01 = pack_bf16x2_exact(lo[0], lo[1]);
+  out23 = pack_bf16x2_exact(hi[0], hi[1]);
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b,
+                                                const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uintx4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Sum over the four lanes {l, l^16, l^32, l^48}.
+__device__ __forceinline__ float sum_over_lane_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Candidate limit of a query row: positions s < limit are candidates.
+__device__ __forceinline__ int candidate_limit(const int32_t* q_pos,
+                                               const int32_t* kv_len, int b,
+                                               int64_t bt, int L) {
+  int lim = L;
+  if (kv_len) lim = min(lim, max(kv_len[b], 0));
+  if (q_pos) lim = min(lim, max(q_pos[bt] + 1, 0));
+  return lim;
+}
+
+}  // namespace sa

@@ -1,0 +1,77 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernel
+// translation units.  Arguments arrive validated; launchers only enqueue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+struct IndexerArgs {
+  const void* q;
+  int q_dtype;
+  const float* w;
+  const void* k;
+  int k_dtype;
+  const float* k_scale;
+  const int32_t* q_pos;
+  const int32_t* kv_len;
+  int B, T, L, HI, dI;
+  float* scores;
+};
+bool indexer_uses_mfma(const IndexerArgs& a);
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
+
+struct TopkArgs {
+  const float* scores;
+  const int32_t* q_pos;
+  const int32_t* kv_len;
+  int B, T, L, k;
+  int32_t* idx;
+  int32_t* count;
+  void* ws;
+};
+constexpr int kTopkMaxK = 4096;
+size_t topk_workspace_bytes(int B, int T, int L, int k);
+bool topk_supported(int L, int k);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+struct MlaArgs {
+  const void* q_lat;
+  const void* q_rope;
+  int dtype;  // q and kv dtype (equal)
+  const void* c_kv;
+  const void* k_rope;
+  int64_t c_stride, r_stride;  // elements
+  const int32_t* idx;
+  int k, B, T, L, H, dc, dR;
+  float sm_scale;
+  float* out;
+  float* lse;
+  void* ws;
+};
+bool mla_uses_mfma(const MlaArgs& a);
+bool mla_supported(const MlaArgs& a);
+size_t mla_workspace_bytes(int dtype, int B, int T, int k, int H, int dc);
+hipError_t launch_mla(const MlaArgs& a, hipStream_t st);
+
+struct BlockArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* krep;
+  int B, L, Hq, Hkv, d, blk, nsel, n_sink, n_win;
+  float sm_scale;
+  float* out;
+  int32_t* blocks_out;
+  void* ws;
+};
+bool block_supported(const BlockArgs& a);
+size_t block_workspace_bytes(int B, int Hq, int L, int nsel, int Hkv, int d, int blk);
+hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d,
+                             int blk, float* krep, hipStream_t st);
+hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st);
+
+}  // namespace sa
