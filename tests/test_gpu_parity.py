@@ -122,7 +122,8 @@ def test_topk_exact_small_integer_workload():
 @pytest.mark.parametrize("L,k,kind", [(5000, 2048, "normal"), (32768, 2048, "ties"),
                                       (32768, 4096, "signed"), (1000, 1, "ties"),
                                       (70000, 2048, "ties"), (131072, 2048, "normal"),
-                                      (40000, 64, "zeros")])
+                                      (40000, 64, "zeros"), (70000, 2048, "narrow"),
+                                      (70000, 2048, "allequal")])
 def test_topk_matches_oracle_bitexact(L, k, kind):
     _announce(f"topk L={L} k={k} {kind}")
     g0 = torch.Generator().manual_seed(L + k)
@@ -131,6 +132,11 @@ def test_topk_matches_oracle_bitexact(L, k, kind):
         s = torch.randn(B, 1, L, generator=g0).abs()
     elif kind == "ties":
         s = torch.randint(0, 40, (B, 1, L), generator=g0).float() * 0.25
+    elif kind == "narrow":
+        # every key shares its top 11 bits: the first bin exceeds what LDS holds
+        s = 1.0 + torch.randint(0, 1024, (B, 1, L), generator=g0).float() * 2.0 ** -20
+    elif kind == "allequal":
+        s = torch.full((B, 1, L), 3.0)
     elif kind == "zeros":
         s = torch.zeros(B, 1, L)
         s[:, :, ::97] = 1.0
@@ -301,3 +307,33 @@ def test_prefill_path_small_causal():
     for t_ in range(L):
         sel = gi[0, t_][gi[0, t_] >= 0]
         assert sel.max() <= t_
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending", "zigzag"])
+def test_mla_bf16_score_ramps(order):
+    # Scores that climb (or fall, or alternate) across the tiles of a split, so
+    # the running maximum moves many times, by steps both inside and beyond the
+    # kernel's rescaling margin; dynamic range ~80 in natural-log units.
+    _announce(f"mla bf16 score ramp {order}")
+    B, L, k, H = 2, 2100, 2048, 64
+    wl = workloads.decode_32k(B=B, L=L, H=H, n_needles=0)
+    kv = wl.kv.float()
+    qr = wl.q_rope.float()
+    ramp = torch.linspace(-40.0, 40.0, L)
+    if order == "descending":
+        ramp = ramp.flip(0)
+    elif order == "zigzag":
+        ramp = ramp * torch.where(torch.arange(L) % 3 == 0, 1.0, -0.5)
+    for b in range(B):
+        u = qr[b, 0].sum(0)
+        u = u / u.norm()
+        # k_rope_j = c_j * u  =>  q_rope_h . k_rope_j = c_j (q_rope_h . u)
+        kv[b, :, wl.dc:] = ramp[:, None] * u[None, :] * (24.0 / max(float((qr[b, 0] @ u).abs().mean()), 1e-3))
+    wl.kv = kv.to(torch.bfloat16)
+    idx = np.stack([np.arange(k) for _ in range(B)])[:, None].astype(np.int32)
+    ql, qrg, kvg, gidx = _cuda(wl.q_lat, wl.q_rope, wl.kv, torch.from_numpy(idx))
+    out, lse = api.sparse_attn_mla_forward(ql, qrg, kvg[..., :wl.dc], kvg[..., wl.dc:], gidx,
+                                           wl.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, idx, wl.sm_scale, dc=wl.dc)
+    assert_attention_close(out, ro, ATTN_ATOL_BF16, lse, rl, lse_atol=2e-3)

@@ -37,15 +37,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t packed) {
   return __builtin_bit_cast(float, packed & 0xffff0000u);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t float_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
-  return float_to_bf16_rne(lo) | (float_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{lo, hi}, bf16x2));
 }
 // Exact packing of two fp32 values that are representable in bf16.
 __device__ __forceinline__ uint32_t pack_bf16x2_exact(float lo, float hi) {
@@ -74,7 +71,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uintx4& v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Sum over the four lanes {l, l^16, l^32, l^48}.
+// Sum / max over the four lanes {l, l^16, l^32, l^48}.
 __device__ __forceinline__ float sum_over_lane_groups(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);

@@ -9,8 +9,11 @@
 //
 // mla_mfma_kernel (bf16, dc = 512, dR = 64): a work-group is four waves of 16
 // heads each and walks a range of the query's slots 32 rows at a time.  The
-// 32 gathered rows (1152 bytes each: 1024 of c_kv, 128 of k_rope) are staged
-// in LDS, double buffered.  Per wave and tile:
+// 32 gathered rows (1152 bytes each: 1024 of c_kv, 128 of k_rope) arrive in
+// LDS by direct global->LDS loads (global_load_lds_dwordx4), four tile
+// buffers deep, so three tiles (108 KB) are in flight while one is consumed:
+// random row gathers are latency-bound and need that depth.  Per wave and
+// tile:
 //   S^T[32 rows x 16 heads] = K[32 x 576] Q^T            (36 MFMA 16x16x32)
 //   online softmax per head (each lane owns one head: a lane's S^T values all
 //   belong to head l%16, so the max, the rescale and the row sums stay in the
@@ -38,13 +41,49 @@ namespace sa {
 // bf16 MFMA path
 // ---------------------------------------------------------------------------
 constexpr int kMlaDc = 512, kMlaDr = 64, kMlaD = kMlaDc + kMlaDr;
-constexpr int kMlaRowB = kMlaD * 2;           // 1152 bytes per gathered row
-constexpr int kMlaLRow = kMlaRowB + 16;       // padded LDS row (bank spread)
-constexpr int kMlaTile = 32;                  // rows per tile
-constexpr int kMlaWaves = 4;                  // 16 heads per wave
-constexpr int kMlaHeadsWg = 16 * kMlaWaves;
-constexpr int kMlaChunksRow = kMlaRowB / 16;  // 72 x 16 bytes
-constexpr int kMlaStage = (kMlaTile * kMlaChunksRow + 64 * kMlaWaves - 1) / (64 * kMlaWaves);
+constexpr int kMlaRowB = kMlaD * 2;              // 1152 bytes per gathered row
+constexpr int kMlaPieces = kMlaRowB / 16;        // 72 pieces of 16 bytes
+constexpr int kMlaTile = 32;                     // rows per tile
+constexpr int kMlaTileB = kMlaTile * kMlaRowB;   // 36864 bytes
+constexpr int kMlaTileLoads = kMlaTileB / 1024;  // 36 wave-wide 16-byte-per-lane loads
+constexpr int kMlaBuf = 4;                       // LDS tiles: 3 in flight + 1 in use
+constexpr int kMlaMaxSplitSlots = 2048;          // index slice of one work-group
+
+// Row r of a tile stores its 16-byte piece p at position p ^ swz(r) (inside
+// the aligned group of 8 pieces, so c_kv and k_rope pieces stay apart).  With
+// swz the Gray code of r's low bits, both the QK reads (16 rows, one piece
+// each) and the PV transpose reads (4 rows x 4 half-pieces per lane group)
+// hit distinct LDS banks.
+__device__ __forceinline__ int row_swz(int r) { return (r ^ (r >> 1)) & 7; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// One wave-wide global->LDS load: lane l's 16 bytes at gbase + voff land at
+// LDS byte lds_base + 16 l.  Issued as inline asm so that the compiler neither
+// tracks it nor inserts its own (whole-queue) waits before LDS reads; the
+// pipeline waits explicitly with wait_vmcnt.  The instruction has no register
+// result.
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+// The same with a full 64-bit per-lane address.
+__device__ __forceinline__ void dma16_addr(const uint8_t* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gaddr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// Work-group barrier without the memory fence of __syncthreads (which would
+// also wait for the tiles still in flight); "memory" keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 struct MlaKernelArgs {
   const uint16_t* q_lat;   // [BT, H, 512]
@@ -55,6 +94,7 @@ struct MlaKernelArgs {
   const int32_t* idx;      // [BT, k]
   int k, T, L, H;
   int nsplit, slots_per_split;
+  int packed;              // k_rope row = c_kv row + 1024 bytes, same stride
   float scale_log2;        // sm_scale * log2(e)
   float* out;              // [BT, H, 512]
   float* lse;              // [BT, H] or null
@@ -62,16 +102,20 @@ struct MlaKernelArgs {
   float* part_ml;          // [BT, H, nsplit, 2]
 };
 
-constexpr int kMlaMaxSplitSlots = 2048;  // index slice of one work-group, kept in LDS
-
-__global__ __launch_bounds__(64 * kMlaWaves, 1) void mla_mfma_kernel(MlaKernelArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kMlaTile * kMlaLRow];
-  __shared__ int spos[kMlaMaxSplitSlots];  // positions of this split, -1 = skip
+// NW waves of 16 heads each; one work-group per (query, head group, KV split).
+// PACKED: k_rope row = c_kv row + 1024 bytes with one stride ([B, L, 576]).
+template <int NW, bool PACKED>
+__global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kMlaBuf][kMlaTileB];
+  __shared__ int spos[kMlaMaxSplitSlots];                  // row to fetch (always valid)
+  __shared__ uint32_t svmask[kMlaMaxSplitSlots / kMlaTile];  // bit r: row r counts
+  __shared__ int sfirst;
 
   // block -> (bt, head group, split); blocks that share (bt, split) are placed
   // on the same XCD (blocks are dealt to the 8 XCDs round-robin) so the head
   // groups' re-reads of the gathered rows hit that XCD's L2.
-  const int hgroups = a.H / kMlaHeadsWg;
+  constexpr int HW = 16 * NW;
+  const int hgroups = a.H / HW;
   const int nblk = gridDim.x;
   int lin = blockIdx.x;
   if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
@@ -82,19 +126,73 @@ __global__ __launch_bounds__(64 * kMlaWaves, 1) void mla_mfma_kernel(MlaKernelAr
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int h = hg * kMlaHeadsWg + wave * 16 + n;  // this lane's head
+  const int h = hg * HW + wave * 16 + n;  // this lane's head
 
   const int j_begin = split * a.slots_per_split;
-  const int j_end = min(a.k, j_begin + a.slots_per_split);
-  const int ntiles = (j_end - j_begin + kMlaTile - 1) / kMlaTile;
-  const int32_t* idxr = a.idx + bt * a.k;
-  // the split's index slice goes to LDS first: row addresses then never wait
-  // on a global load
-  for (int j = tid; j < ntiles * kMlaTile; j += 64 * kMlaWaves) {
-    const int s = j_begin + j < j_end ? idxr[j_begin + j] : -1;
-    spos[j] = (s >= 0 && s < a.L) ? s : -1;
+  const int nslots = max(0, min(a.k, j_begin + a.slots_per_split) - j_begin);
+  const int32_t* idxr = a.idx + bt * a.k + j_begin;
+
+  // ---- the split's index slice -> LDS; skipped slots fetch a valid row ----
+  if (tid == 0) sfirst = 0x7fffffff;
+  __syncthreads();
+  for (int j = tid; j < nslots; j += 64 * NW) {
+    const int s = idxr[j];
+    if (s >= 0 && s < a.L) atomicMin(&sfirst, s);
   }
   __syncthreads();
+  const int first = sfirst;
+  const int ntiles = first == 0x7fffffff ? 0 : (nslots + kMlaTile - 1) / kMlaTile;
+  for (int j0 = 0; j0 < ntiles * kMlaTile; j0 += 64 * NW) {  // uniform trip count
+    const int j = j0 + tid;
+    const int s = j < nslots ? idxr[j] : -1;
+    const bool ok = s >= 0 && s < a.L;
+    if (j < ntiles * kMlaTile) spos[j] = ok ? s : first;
+    const uint64_t m = __ballot(ok);  // 64 slots = two tiles
+    if (lane == 0 && j < ntiles * kMlaTile) {
+      svmask[j / kMlaTile] = (uint32_t)m;
+      if (j / kMlaTile + 1 < ntiles) svmask[j / kMlaTile + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  __syncthreads();
+
+  // ---- tile fetch: wave w issues the 1 KB pieces q = w, w + NW, ... ----
+  // Lane l of load i fills 16-byte slot c = 64 q + l of the tile: row c / 72,
+  // position c % 72, which holds piece (c % 72) ^ swz(row).  Rows and pieces
+  // are the same for every tile, so they are computed once; per load only the
+  // gathered row's position changes.  The packed layout (k_rope right after
+  // c_kv in one row, as a [B, L, 576] cache) needs one base and one stride; a
+  // split cache takes the piece's own base.
+  static_assert(kMlaTileLoads % NW == 0, "equal loads per wave");
+  constexpr int NLD = kMlaTileLoads / NW;  // loads per tile and wave
+  const uint8_t* cb = a.c_kv + (int64_t)b * a.L * a.c_stride_b;
+  const uint8_t* rb = a.k_rope + (int64_t)b * a.L * a.r_stride_b;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tiles[0][0];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t drow[NLD], dpiece[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int c = 64 * (wv + NW * i) + lane;
+    const int r = c / kMlaPieces, pp = c % kMlaPieces;
+    drow[i] = 4 * r;                  // byte offset into a tile's slice of spos
+    dpiece[i] = 16 * (pp ^ row_swz(r));
+  }
+  auto issue = [&](int tl) {
+    const uint32_t dst = lds0 + (uint32_t)((tl % kMlaBuf) * kMlaTileB);
+    const uint8_t* sp = (const uint8_t*)spos + 4 * tl * kMlaTile;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t s = *(const uint32_t*)(sp + drow[i]);
+      const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NW * i);
+      if constexpr (PACKED) {
+        dma16(cb, s * (uint32_t)a.c_stride_b + dpiece[i], ldst);
+      } else {
+        const bool rope = dpiece[i] >= 1024u;
+        const uint8_t* base = rope ? rb : cb;
+        const uint32_t stride = rope ? (uint32_t)a.r_stride_b : (uint32_t)a.c_stride_b;
+        dma16_addr(base + (s * stride + (dpiece[i] & 1023u)), ldst);
+      }
+    }
+  };
 
   // Q^T operand: qb[ks] = q[h][32 ks + 8 g .. +8], ks < 16 from q_lat, 16..17 q_rope
   bf16x8 qb[18];
@@ -106,119 +204,142 @@ __global__ __launch_bounds__(64 * kMlaWaves, 1) void mla_mfma_kernel(MlaKernelAr
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) qb[16 + ks] = as_bf16x8(*(const uintx4*)(qr + 32 * ks + 8 * g));
   }
+  wait_vmcnt<0>();  // Q is in registers before the tile loads start counting
+#pragma unroll
+  for (int t = 0; t < kMlaBuf - 1; ++t)
+    if (t < ntiles) issue(t);
 
   floatx4 o[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- staging: chunk c = tid + 256 i -> row c / 72, 16-byte piece c % 72 ----
-  uintx4 stage[kMlaStage];
-  auto gload = [&](int tl) {
+  // per-lane byte offsets of the swizzled reads
+  const int mq = row_swz(n);                 // QK rows 16 jt + n
+  const int qoff0 = 16 * (g ^ mq), qoff1 = 16 * ((4 + g) ^ mq);
+  const int R = 4 * g + (n >> 2);            // PV rows R and R + 16
+  const int mv = row_swz(R);
+  int voff[4];
 #pragma unroll
-    for (int i = 0; i < kMlaStage; ++i) {
-      const int c = tid + 64 * kMlaWaves * i;
-      stage[i] = uintx4{0u, 0u, 0u, 0u};
-      if (c < kMlaTile * kMlaChunksRow) {
-        const int r = c / kMlaChunksRow, p = c % kMlaChunksRow;
-        const int s = spos[tl * kMlaTile + r];
-        if (s >= 0) {
-          const int64_t row = (int64_t)b * a.L + s;
-          const uint8_t* src = p < 64 ? a.c_kv + row * a.c_stride_b + 16 * p
-                                      : a.k_rope + row * a.r_stride_b + 16 * (p - 64);
-          stage[i] = *(const uintx4*)src;
+  for (int d4 = 0; d4 < 4; ++d4) voff[d4] = 16 * ((2 * d4 + ((n & 3) >> 1)) ^ mv) + 8 * (n & 1);
+
+  for (int tl = 0; tl < ntiles; ++tl) {
+    // this wave's part of tile tl landed (loads return in order; the tiles
+    // issued after it may still be in flight)
+    const int ahead = min(kMlaBuf - 2, ntiles - 1 - tl);
+    if (ahead >= 2)
+      wait_vmcnt<2 * NLD>();
+    else if (ahead == 1)
+      wait_vmcnt<NLD>();
+    else
+      wait_vmcnt<0>();
+    wait_lgkm0();
+    lds_barrier();  // every wave's part landed; tile tl-1 no longer read
+    if (tl + kMlaBuf - 1 < ntiles) issue(tl + kMlaBuf - 1);
+    const uint8_t* tb = tiles[tl % kMlaBuf];
+
+    // S^T[jt]: rows 16 jt + 4 g + r, head n.  The two row blocks are two
+    // independent accumulator chains, interleaved, with the K operands of the
+    // next k-step loaded while the current one multiplies.
+    floatx4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* r0 = tb + n * kMlaRowB;
+      const uint8_t* r1 = r0 + 16 * kMlaRowB;
+      auto kop = [&](const uint8_t* rp, int ks) {
+        return *(const uintx4*)(rp + 128 * (ks >> 1) + ((ks & 1) ? qoff1 : qoff0));
+      };
+      uintx4 a0 = kop(r0, 0), a1 = kop(r1, 0);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        uintx4 b0, b1;
+        if (ks + 1 < 18) {
+          b0 = kop(r0, ks + 1);
+          b1 = kop(r1, ks + 1);
+        }
+        st0 = mfma16x16x32(as_bf16x8(a0), qb[ks], st0);
+        st1 = mfma16x16x32(as_bf16x8(a1), qb[ks], st1);
+        if (ks + 1 < 18) {
+          a0 = b0;
+          a1 = b1;
         }
       }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kMlaStage; ++i) {
-      const int c = tid + 64 * kMlaWaves * i;
-      if (c < kMlaTile * kMlaChunksRow) {
-        const int r = c / kMlaChunksRow, p = c % kMlaChunksRow;
-        *(uintx4*)(&tile[buf][r * kMlaLRow + 16 * p]) = stage[i];
-      }
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int tl = 0; tl < ntiles; ++tl) {
-    const int buf = tl & 1;
-    if (tl + 1 < ntiles) gload(tl + 1);
-    const uint8_t* tb = tile[buf];
-
-    // S^T[jt]: rows 16 jt + 4 g + r, head n
-    floatx4 st[2];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* rowp = tb + (16 * jt + n) * kMlaLRow + 16 * g;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks)
-        acc = mfma16x16x32(as_bf16x8(*(const uintx4*)(rowp + 64 * ks)), qb[ks], acc);
-      st[jt] = acc;
     }
     // scale to log2 units, mask skipped slots, tile max per head
     float x[8];
     float mt = -INFINITY;
+    const uint32_t vm = svmask[tl] >> (4 * g);
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * jt + 4 * g + r;
-        const float v = spos[tl * kMlaTile + row] >= 0 ? st[jt][r] * a.scale_log2 : -INFINITY;
-        x[4 * jt + r] = v;
-        mt = fmaxf(mt, v);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float v0 = (vm >> r) & 1u ? st0[r] * a.scale_log2 : -INFINITY;
+      const float v1 = (vm >> (16 + r)) & 1u ? st1[r] * a.scale_log2 : -INFINITY;
+      x[r] = v0;
+      x[4 + r] = v1;
+      mt = fmaxf(mt, fmaxf(v0, v1));
+    }
     mt = max_over_lane_groups(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);  // 0 while nothing seen yet
+    // Lazy rescaling: the reference max m_run moves only when a score exceeds
+    // it by more than 8 (log2 units), so the weights exp2(x - m_run) stay below
+    // 256 and the fp32 accumulators are rescaled only on such jumps.
+    const bool grow = mt > m_run + 8.f;
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // 0 at first
+      if (grow) m_run = mt;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) o[i] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits, so
     // the product stays at fp32-level accuracy while the MFMAs stay bf16.
     uint32_t pbh[4], pbl[4];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = exp2f(x[e] - m_use), p1 = exp2f(x[e + 1] - m_use);
+      const float p0 = __builtin_amdgcn_exp2f(x[e] - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(x[e + 1] - m_use);
       psum += p0 + p1;
       const uint32_t hi = pack_bf16x2_rne(p0, p1);
       pbh[e / 2] = hi;
       pbl[e / 2] = pack_bf16x2_rne(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-    }
+    l_run += psum;
     const bf16x8 pBh = __builtin_bit_cast(bf16x8, uintx4{pbh[0], pbh[1], pbh[2], pbh[3]});
     const bf16x8 pBl = __builtin_bit_cast(bf16x8, uintx4{pbl[0], pbl[1], pbl[2], pbl[3]});
-    // V^T operand rows: 4 g + (lane%16)/4 and 16 + 4 g + (lane%16)/4, columns
-    // 16 dt + 4 (lane%4) .. +3  (see the transpose-read note in common.hpp)
-    const uint8_t* v0 = tb + (4 * g + (n >> 2)) * kMlaLRow + 8 * (n & 3);
-    const uint8_t* v1 = v0 + 16 * kMlaLRow;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
+    // V^T operand: rows R..R+3 -> lane group g, column 16 dt + lane%16 (see the
+    // transpose-read note in common.hpp); piece 2 dt + (lane%4)/2, half lane%2.
+    // Operands of d-tile dt+1 load while dt multiplies; the hi and lo products
+    // of one accumulator are separated by the other d-tile's product.
+    const uint8_t* v0 = tb + R * kMlaRowB;
+    const uint8_t* v1 = v0 + 16 * kMlaRowB;
+    auto vop = [&](int dt) {
+      const int off = 128 * (dt >> 2) + voff[dt & 3];
       shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (shortx4 __attribute__((address_space(3)))*)(v0 + 32 * dt));
+          (shortx4 __attribute__((address_space(3)))*)(v0 + off));
       shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (shortx4 __attribute__((address_space(3)))*)(v1 + 32 * dt));
-      const bf16x8 vA = __builtin_bit_cast(
+          (shortx4 __attribute__((address_space(3)))*)(v1 + off));
+      return __builtin_bit_cast(
           bf16x8, uintx4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))});
-      o[dt] = mfma16x16x32(vA, pBh, o[dt]);
-      o[dt] = mfma16x16x32(vA, pBl, o[dt]);
+    };
+    bf16x8 va = vop(0), vb = vop(1);
+#pragma unroll
+    for (int dt = 0; dt < 32; dt += 2) {
+      bf16x8 na, nb;
+      if (dt + 2 < 32) {
+        na = vop(dt + 2);
+        nb = vop(dt + 3);
+      }
+      o[dt] = mfma16x16x32(va, pBh, o[dt]);
+      o[dt + 1] = mfma16x16x32(vb, pBh, o[dt + 1]);
+      o[dt] = mfma16x16x32(va, pBl, o[dt]);
+      o[dt + 1] = mfma16x16x32(vb, pBl, o[dt + 1]);
+      if (dt + 2 < 32) {
+        va = na;
+        vb = nb;
+      }
     }
-    if (tl + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- finish ----
@@ -406,12 +527,17 @@ static size_t vector_lds_bytes(int H, int dc, int dR) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
+constexpr int kMlaWaves = 4;  // 64 heads per work-group
+constexpr int kMlaHeadsWg = 16 * kMlaWaves;
+
 bool mla_uses_mfma(const MlaArgs& a) {
   return a.dtype == SA_BF16 && a.dc == kMlaDc && a.dR == kMlaDr && a.H % kMlaHeadsWg == 0;
 }
 
 bool mla_supported(const MlaArgs& a) {
-  if (mla_uses_mfma(a)) return true;
+  // the bf16 path addresses a sequence's rows with 32-bit byte offsets
+  if (mla_uses_mfma(a))
+    return (int64_t)a.L * a.c_stride * 2 < (1LL << 32) && (int64_t)a.L * a.r_stride * 2 < (1LL << 32);
   if (a.dc > 512 || a.dR > 64 || a.dR < 0 || a.dc < 1) return false;
   if ((int64_t)a.H * a.dc > 256 * kVecMaxOut) return false;
   return vector_lds_bytes(a.H, a.dc, a.dR) <= 64 * 1024;
@@ -447,6 +573,8 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
     m.k_rope = (const uint8_t*)a.k_rope;
     m.c_stride_b = a.c_stride * 2;
     m.r_stride_b = a.r_stride * 2;
+    m.packed = a.c_stride == a.r_stride &&
+               (const uint8_t*)a.k_rope == (const uint8_t*)a.c_kv + 2 * kMlaDc;
     m.idx = a.idx;
     m.k = a.k;
     m.T = a.T;
@@ -462,7 +590,10 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
       m.part_ml = m.part_o + bt * a.H * m.nsplit * kMlaDc;
     }
     const int64_t nblk = bt * (a.H / kMlaHeadsWg) * m.nsplit;
-    mla_mfma_kernel<<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
+    if (m.packed)
+      mla_mfma_kernel<kMlaWaves, true><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
+    else
+      mla_mfma_kernel<kMlaWaves, false><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || m.nsplit == 1) return e;
     mla_combine_kernel<<<(unsigned)(bt * a.H), 128, 0, st>>>(m.part_o, m.part_ml, m.nsplit,
