@@ -92,6 +92,44 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ---- global->LDS DMA and explicit waits ----
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// One wave-wide global->LDS load: lane l's 16 bytes at gbase + voff land at
+// LDS byte lds_base + 16 l.  Issued as inline asm so that the compiler neither
+// tracks it nor inserts its own (whole-queue) waits before LDS reads; the
+// pipeline waits explicitly with wait_vmcnt.  The instruction has no register
+// result.
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+// The same with a full 64-bit per-lane address.
+__device__ __forceinline__ void dma16_addr(const uint8_t* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gaddr)
+               : "memory", "m0");
+}
+// One wave-wide global->LDS load of 4 bytes per lane: lane l's dword at
+// gbase + voff lands at LDS byte lds_base + 4 l.
+__device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// Work-group barrier without the memory fence of __syncthreads (which would
+// also wait for the tiles still in flight); "memory" keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Candidate limit of a query row: positions s < limit are candidates.
 __device__ __forceinline__ int candidate_limit(const int32_t* q_pos,
                                                const int32_t* kv_len, int b,

@@ -11,22 +11,29 @@
 //     NaN and -inf become key 0, "not a candidate").  Wave w holds positions
 //     [2048 w, 2048 w + 2048) in registers, loaded as 16-byte vectors: lane l,
 //     round i, element e is position 2048 w + 4 (l + 64 i) + e.
-//  2. tau = the k-th largest key.  The first histogram digit is fitted to the
-//     row: d = (key - min key) >> sh with sh chosen so that the key range
-//     spans at most 2048 bins.  Index scores share their sign and exponent,
-//     so fixed high-bit digits would pile most keys onto a handful of LDS
-//     addresses and serialise the atomics.  A block scan from the top finds
-//     the bin holding rank k; only that bin's keys (block-scan compacted into
-//     LDS) take part in the passes over the remaining sh bits.
-//  3. Packed (greater-than-tau, equal-to-tau) counts, scanned over the block
-//     in position order, give every selected key its output slot and its
-//     rank among the ties: keys > tau and the first k - count(> tau) keys
-//     == tau are placed in ascending position order in LDS, then written out
-//     with coalesced stores.
+//  2. tau = the k-th largest key.  Keys are binned by a digit fitted to the
+//     row, d = (key - min key) >> sh, with sh chosen so that the key range
+//     spans at most 2048 bins (index scores share sign and exponent, so fixed
+//     high-bit digits would pile the keys onto a few LDS words).
+//     a. A histogram of 1024 sampled keys brackets the rank-k bin with a
+//        margin of four standard deviations of the sample rank.
+//     b. One pass over all keys counts, without atomics, the keys above and
+//        inside the bracket.  If rank k falls outside it, a histogram of all
+//        keys names the exact bin instead.
+//     c. The bracket's keys are compacted into LDS (block scan) and radix
+//        passes of up to 11 bits over them find tau and the number of keys
+//        equal to tau that are taken.
+//  3. Per-round (greater-than-tau, equal-to-tau) counts, prefix-summed over
+//     the block in position order with ballots, give every selected key its
+//     output slot and its rank among the ties: keys > tau and the first
+//     k - count(> tau) keys == tau are placed in ascending position order in
+//     LDS, then written out with coalesced stores.
 // Rows longer than 32768 positions are cut into 32768-position chunks; each
 // chunk keeps its own top-k (a superset of its share of the row's top-k under
 // the same rule), and a second launch selects from the chunks' candidates,
 // which are laid out in ascending position order, so the tie rule carries over.
+#include <math.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,9 +41,12 @@ namespace sa {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kTkSeg = 32;
+constexpr int kTkSeg = 32;                   // keys per thread
+constexpr int kTkRounds = kTkSeg / 4;        // 16-byte loads per thread
 constexpr int kTkRow = kTkThreads * kTkSeg;  // 32768 positions per work-group
+constexpr int kTkWaveSpan = kTkRow / kTkWaves;
 constexpr int kTkBins = 2048;
+constexpr int kTkAux = 5120;  // bracket candidates held in LDS (>= kTopkMaxK)
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -50,15 +60,56 @@ __device__ __forceinline__ float key_score(uint32_t key) {
   return __builtin_bit_cast(float, u);
 }
 
+// ---- wave primitives on DPP (no LDS round trip) ----
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp0(int v) {  // lanes without a source read 0
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+// Inclusive prefix sum over the 64 lanes: row_shr 1/2/4/8 inside each row of
+// 16, then row_bcast 15 and 31 carry the row totals upward.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += dpp0<0x111>(x);
+  x += dpp0<0x112>(x);
+  x += dpp0<0x114>(x);
+  x += dpp0<0x118>(x);
+  x += dpp0<0x142, 0xa>(x);
+  x += dpp0<0x143, 0xc>(x);
+  return x;
+}
+__device__ __forceinline__ int wave_total(int x) {
+  return __builtin_amdgcn_readlane(wave_scan_incl(x), 63);
+}
+// Minimum / maximum over the 64 lanes: quad and mirror exchanges inside each
+// row of 16, then the four row results through scalar registers.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+// Set bits of `m` held by lanes below this one.
+__device__ __forceinline__ int mbcnt(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Inclusive block scan (sum) of one int per thread; `red` holds kTkWaves ints.
 // Returns the inclusive prefix; `total` receives the block sum.
 __device__ __forceinline__ int block_scan_incl(int x, int* red, int& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  x = wave_scan_incl(x);
   __syncthreads();  // red may still be read by a previous scan
   if (lane == 63) red[wave] = x;
   __syncthreads();
@@ -66,54 +117,61 @@ __device__ __forceinline__ int block_scan_incl(int x, int* red, int& total) {
   total = 0;
 #pragma unroll
   for (int w = 0; w < kTkWaves; ++w) {
-    int v = red[w];
-    if (w < wave) before += v;
+    const int v = red[w];
+    before += w < wave ? v : 0;
     total += v;
   }
   return x + before;
 }
 
+// Block sum: every thread receives the total.
 __device__ __forceinline__ int block_sum(int x, int* red) {
-  int total;
-  block_scan_incl(x, red, total);
+  const int t = wave_total(x);
+  __syncthreads();  // red may still be read by a previous reduction
+  if (lane_id() == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) total += red[w];
   return total;
 }
 
-// The bin of `hist` (2048 bins) holding rank krem counted from the top;
-// writes (bin, keys in higher bins) to found[0..1].  1024 threads, thread t
-// owning bins 2047-2t and 2046-2t.  Starts with a barrier (the histogram is
-// complete) and ends with one (found is visible).
-__device__ __forceinline__ void find_rank_bin(const int* hist, int krem, int* red, int* found) {
+// Bins of `hist` (2048 bins) holding ranks r0 <= r1 counted from the top.
+// Thread t owns bins 2047-2t and 2046-2t.  found[0..1] = (bin of r0, keys in
+// higher bins), found[2] = bin of r1, where ranks(total, r0, r1) sets the
+// ranks from the histogram's total; a rank outside [1, total] gives bin -1.
+// Starts with a barrier (the histogram is complete) and ends with one (found
+// is visible).
+template <class Ranks>
+__device__ __forceinline__ void find_rank_bins(const int* hist, Ranks ranks, int* red,
+                                               int* found) {
   __syncthreads();
   const int tid = threadIdx.x;
+  if (tid == 0) {  // a rank beyond the total leaves these: bin -1, above 0
+    found[0] = found[2] = -1;
+    found[1] = 0;
+  }
   const int bhi = kTkBins - 1 - 2 * tid, blo = bhi - 1;
   const int hhi = hist[bhi], hlo = hist[blo];
   int total;
   const int incl = block_scan_incl(hhi + hlo, red, total);
   const int above = incl - hhi - hlo;
-  if (above < krem && krem <= above + hhi) {
+  int r0, r1;
+  ranks(total, r0, r1);
+  if (above < r0 && r0 <= above + hhi) {
     found[0] = bhi;
     found[1] = above;
-  } else if (above + hhi < krem && krem <= above + hhi + hlo) {
+  } else if (above + hhi < r0 && r0 <= above + hhi + hlo) {
     found[0] = blo;
     found[1] = above + hhi;
   }
+  if (above < r1 && r1 <= above + hhi) {
+    found[2] = bhi;
+  } else if (above + hhi < r1 && r1 <= above + hhi + hlo) {
+    found[2] = blo;
+  }
   __syncthreads();
 }
-
-struct TopkRowArgs {
-  const float* scores;   // direct rows: scores[bt * L + s]
-  const int32_t* q_pos;
-  const int32_t* kv_len;
-  int T, L, k;
-  int nchunks;           // chunks per row of the first launch
-  // first launch with nchunks > 1: candidates per (row, chunk)
-  float* cand_score;     // [rows][nchunks][k]
-  int32_t* cand_pos;
-  // final output
-  int32_t* idx;          // [rows][k]
-  int32_t* count;        // [rows] or null
-};
 
 // hist[d] += 1 for every lane with `valid`.  When all valid lanes of the wave
 // share one bin, one lane adds the whole count instead of 64 lanes hitting
@@ -130,17 +188,40 @@ __device__ __forceinline__ void hist_add(int* hist, uint32_t d, bool valid) {
   }
 }
 
+struct TopkRowArgs {
+  const float* scores;   // direct rows: scores[bt * L + s]
+  const int32_t* q_pos;
+  const int32_t* kv_len;
+  int T, L, k;
+  int nchunks;           // chunks per row of the first launch
+  // first launch with nchunks > 1: candidates per (row, chunk)
+  float* cand_score;     // [rows][nchunks][k]
+  int32_t* cand_pos;
+  // final output
+  int32_t* idx;          // [rows][k]
+  int32_t* count;        // [rows] or null
+};
+
 // MERGE = false: virtual row = positions [chunk*kTkRow, ...) of a score row.
 // MERGE = true : virtual row = the nchunks*k candidates of a row.
+//
+// Code size matters here: a work-group runs its row once, usually on a CU
+// whose instruction cache is cold, so every 64 bytes of straight-line code
+// cost a fetch from L2.  The keys therefore live in LDS, arrive there by
+// global->LDS DMA (no registers, no unrolling), and every phase is a short
+// loop; all histogram rounds share one rank search.
 template <bool MERGE>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
-  __shared__ uint32_t cand[kTkRow];  // rank-k bin candidates, then the output
+  __shared__ uint4 keys4[kTkRow / 4];  // the row's keys by position
+  __shared__ uint32_t aux[kTkAux];     // bracket candidates, then output positions
   __shared__ int hist[kTkBins];
   __shared__ int red[kTkWaves];
   __shared__ uint32_t rmin[kTkWaves], rmax[kTkWaves];
-  __shared__ int found[2];
+  __shared__ int found[4];
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(keys4);
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bt = blockIdx.y;
   const int chunk = blockIdx.x;
   const int k = a.k;
@@ -174,76 +255,58 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
     out_count = a.count ? a.count + bt : nullptr;
   }
 
-  // ---- keys to registers: kr[4 i + e] is position wbase + 4 (lane + 64 i) + e
-  const int wbase = wave * (kTkRow / kTkWaves);
-  uint32_t kr[kTkSeg];
+  // ---- scores into LDS by DMA; wave w fills positions [2048 w, 2048 w + 2048)
+  const int wbase4 = wave * (kTkWaveSpan / 4);  // in 16-byte units
+  const uint32_t lds_keys = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)&keys4[0];
+  const uint8_t* gsrc = reinterpret_cast<const uint8_t*>(src);
   if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-    float4 f[kTkSeg / 4];
-#pragma unroll
-    for (int i = 0; i < kTkSeg / 4; ++i) {
-      const int p = wbase + 4 * (lane + 64 * i);
-      f[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (p + 3 < n) f[i] = *reinterpret_cast<const float4*>(src + p);
+    for (int i = 0; i < kTkRounds; ++i) {  // 16 bytes per lane, 1 KB per wave
+      const int u = wbase4 + 64 * i;
+      if (4 * (u + lane) + 3 < n) dma16(gsrc, 16u * (uint32_t)(u + lane), lds_keys + 16u * (uint32_t)u);
     }
-#pragma unroll
-    for (int i = 0; i < kTkSeg / 4; ++i) {
-      const int p = wbase + 4 * (lane + 64 * i);
-      float v[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
-      if (p < n && p + 3 >= n) {  // the row's ragged end
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = p + e < n ? src[p + e] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kr[4 * i + e] = p + e < n ? score_key(v[e]) : 0u;
-    }
+    const int n4 = n & ~3;  // the ragged end: up to 3 scores, one dword each
+    if (wave == 0 && lane < n - n4) dma4(gsrc, 4u * (uint32_t)(n4 + lane), lds_keys + 4u * (uint32_t)n4);
   } else {
-    float f[kTkSeg];
-#pragma unroll
-    for (int i = 0; i < kTkSeg / 4; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = wbase + 4 * (lane + 64 * i) + e;
-        f[4 * i + e] = p < n ? src[p] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kTkSeg / 4; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = wbase + 4 * (lane + 64 * i) + e;
-        kr[4 * i + e] = p < n ? score_key(f[4 * i + e]) : 0u;
-      }
+    for (int i = 0; i < 4 * kTkRounds; ++i) {  // 4 bytes per lane
+      const int p = 4 * wbase4 + 64 * i;
+      if (p + lane < n) dma4(gsrc, 4u * (uint32_t)(p + lane), lds_keys + 4u * (uint32_t)p);
     }
   }
+  wait_vmcnt<0>();
+  lds_barrier();
 
-  // ---- count, min and max of the valid keys ----
+  // ---- scores -> keys in place (positions >= n -> 0); count, min, max ----
   int n_valid;
   uint32_t kmin, kmax;
   {
     uint32_t mn = 0xffffffffu, mx = 0u;
     int nv = 0;
+#pragma unroll 2
+    for (int i = 0; i < kTkRounds; ++i) {
+      const int u = wbase4 + lane + 64 * i;
+      uint4 q = keys4[u];
+      uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int j = 0; j < kTkSeg; ++j) {
-      nv += kr[j] != 0u;
-      mn = kr[j] ? min(mn, kr[j]) : mn;
-      mx = max(mx, kr[j]);
+      for (int e = 0; e < 4; ++e) {
+        kk[e] = 4 * u + e < n ? score_key(__builtin_bit_cast(float, kk[e])) : 0u;
+        nv += kk[e] != 0u;
+        mn = kk[e] ? min(mn, kk[e]) : mn;
+        mx = max(mx, kk[e]);
+      }
+      keys4[u] = make_uint4(kk[0], kk[1], kk[2], kk[3]);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      nv += __shfl_xor(nv, o);
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    }
+    nv = wave_total(nv);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
     if (lane == 0) {
       red[wave] = nv;
       rmin[wave] = mn;
       rmax[wave] = mx;
     }
-    __syncthreads();
+    __syncthreads();  // also publishes the keys
     n_valid = 0;
     kmin = 0xffffffffu;
     kmax = 0u;
-#pragma unroll
     for (int w = 0; w < kTkWaves; ++w) {
       n_valid += red[w];
       kmin = min(kmin, rmin[w]);
@@ -257,108 +320,194 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
   if (n_valid > k) {
     const uint32_t range = kmax - kmin;
     const int sh = max(0, 32 - __clz(range) - 11);  // (range >> sh) < 2048
-    for (int i = tid; i < kTkBins; i += kTkThreads) hist[i] = 0;
-    __syncthreads();
+    const float p_sel = (float)k / (float)n_valid;
+    enum { kSample, kAll, kCand, kFilter };
+    int mode = kSample;
+    int krem = k, ncand = 0, top = -1, in_me = 0;
+    uint32_t lo_key = 0u, hi_key = 0u, prefix = 0u, pmask = 0u;  // bracket [lo_key, hi_key]
+    for (;;) {
+      __syncthreads();  // the previous round's bins have been read
+      for (int i = tid; i < kTkBins; i += kTkThreads) hist[i] = 0;
+      __syncthreads();
+      int s2 = 0;
+      uint32_t dmask = 0u;
+      if (mode == kSample) {
+        // one key per lane, spread over the wave's eight rounds
+        const uint32_t key = keys[4 * (wbase4 + lane + 64 * (lane & 7)) + ((lane >> 3) & 3)];
+        hist_add(hist, (key - kmin) >> sh, key != 0u);
+      } else if (mode == kAll) {
+        #pragma unroll 1
+        for (int i = 0; i < kTkRounds; ++i) {
+          const uint4 q = keys4[wbase4 + lane + 64 * i];
+          const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int j = 0; j < kTkSeg; ++j) hist_add(hist, (kr[j] - kmin) >> sh, kr[j] != 0u);
-    find_rank_bin(hist, k, red, found);
-    const uint32_t bin = (uint32_t)found[0];
-    int krem = k - found[1];
-    const uint32_t lo = kmin + (bin << sh);
-    uint32_t prefix = 0u, pmask = 0u;  // over key - lo, bits below sh
-    if (sh > 0) {
-      // the bin's keys (as offsets from lo) into LDS, block-scan compacted
-      int mc = 0;
-#pragma unroll
-      for (int j = 0; j < kTkSeg; ++j) mc += kr[j] != 0u && ((kr[j] - kmin) >> sh) == bin;
-      int ncand;
-      int slot = block_scan_incl(mc, red, ncand) - mc;
-      if (mc) {
-#pragma unroll
-        for (int j = 0; j < kTkSeg; ++j)
-          if (kr[j] != 0u && ((kr[j] - kmin) >> sh) == bin) cand[slot++] = kr[j] - lo;
-      }
-      for (int top = sh - 1; top >= 0;) {
-        const int width = min(11, top + 1), s2 = top + 1 - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        __syncthreads();  // candidates written / previous pass's bins read
-        for (int i = tid; i < kTkBins; i += kTkThreads) hist[i] = 0;
-        __syncthreads();
-        const int nit = (ncand + kTkThreads - 1) / kTkThreads;
-        for (int it = 0; it < nit; ++it) {
-          const int j = tid + it * kTkThreads;
-          const uint32_t c = j < ncand ? cand[j] : 0u;
-          hist_add(hist, (c >> s2) & dmask, j < ncand && (c & pmask) == prefix);
+          for (int e = 0; e < 4; ++e) hist_add(hist, (kk[e] - kmin) >> sh, kk[e] != 0u);
         }
-        find_rank_bin(hist, krem, red, found);
-        prefix |= (uint32_t)found[0] << s2;
-        pmask |= dmask << s2;
-        krem -= found[1];
-        top = s2 - 1;
+      } else {
+        const int width = min(11, top + 1);
+        s2 = top + 1 - width;
+        dmask = (1u << width) - 1u;
+        if (mode == kCand) {
+    #pragma unroll 1
+      for (int j0 = 0; j0 < ncand; j0 += kTkThreads) {
+            const int j = j0 + tid;
+            const uint32_t c = j < ncand ? aux[j] : 0u;
+            hist_add(hist, (c >> s2) & dmask, j < ncand && (c & pmask) == prefix);
+          }
+        } else {  // kFilter: the bracket outgrew aux; filter the whole row
+          #pragma unroll 1
+          for (int i = 0; i < kTkRounds; ++i) {
+            const uint4 q = keys4[wbase4 + lane + 64 * i];
+            const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t c = kk[e] - lo_key;
+              const bool in = kk[e] != 0u && kk[e] >= lo_key && kk[e] <= hi_key &&
+                              (c & pmask) == prefix;
+              hist_add(hist, (c >> s2) & dmask, in);
+            }
+          }
+        }
       }
+      find_rank_bins(
+          hist,
+          [&](int m, int& r0, int& r1) {
+            if (mode == kSample) {  // four standard deviations of the sample rank
+              const float mean = p_sel * (float)m;
+              const float margin = 4.f * sqrtf(mean * (1.f - p_sel)) + 2.f;
+              r0 = max(1, (int)floorf(mean - margin));
+              r1 = min(m, (int)ceilf(mean + margin));
+            } else {
+              r0 = r1 = krem;
+            }
+          },
+          red, found);
+
+      if (mode == kSample || mode == kAll) {
+        // bins as unsigned: an empty sample gives 0xffffffff, so that nothing
+        // is above or inside and the check below falls back to kAll
+        uint32_t b_hi = (uint32_t)found[0], b_lo = (uint32_t)found[2];
+        int above, inside;
+        if (mode == kSample) {
+          int ab = 0, in = 0;
+          #pragma unroll 1
+          for (int i = 0; i < kTkRounds; ++i) {
+            const uint4 q = keys4[wbase4 + lane + 64 * i];
+            const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t d = (kk[e] - kmin) >> sh;
+              ab += kk[e] != 0u && d > b_hi;
+              in += kk[e] != 0u && d >= b_lo && d <= b_hi;
+            }
+          }
+          // packed: above < 32768 (bin b_hi holds a sampled key), inside <= 32768
+          const int both = block_sum((ab << 16) | in, red);
+          above = both >> 16;
+          inside = both & 0xffff;
+          in_me = in;
+          if (!(above < k && k <= above + inside)) {
+            mode = kAll;
+            continue;
+          }
+        } else {
+          b_hi = b_lo = (uint32_t)found[0];
+          above = found[1];
+          inside = hist[b_hi];  // the bins are only cleared after a barrier
+          in_me = -1;           // not counted per thread
+        }
+        krem = k - above;
+        lo_key = kmin + (b_lo << sh);
+        const uint64_t crange = ((uint64_t)(b_hi - b_lo + 1) << sh) - 1u;  // largest offset
+        hi_key = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)lo_key + crange);
+        top = crange ? 63 - __clzll((long long)crange) : -1;
+        if (top < 0) break;  // the bracket is a single key value
+        if (inside > kTkAux) {
+          mode = kFilter;
+          continue;
+        }
+        // the bracket's keys, as offsets from lo_key, into aux
+        if (in_me < 0) {
+          in_me = 0;
+          #pragma unroll 1
+          for (int i = 0; i < kTkRounds; ++i) {
+            const uint4 q = keys4[wbase4 + lane + 64 * i];
+            in_me += (q.x != 0u && q.x >= lo_key && q.x <= hi_key) +
+                     (q.y != 0u && q.y >= lo_key && q.y <= hi_key) +
+                     (q.z != 0u && q.z >= lo_key && q.z <= hi_key) +
+                     (q.w != 0u && q.w >= lo_key && q.w <= hi_key);
+          }
+        }
+        int slot = block_scan_incl(in_me, red, ncand) - in_me;
+        #pragma unroll 1
+        for (int i = 0; i < kTkRounds && in_me > 0; ++i) {
+          const uint4 q = keys4[wbase4 + lane + 64 * i];
+          const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kk[e] != 0u && kk[e] >= lo_key && kk[e] <= hi_key) aux[slot++] = kk[e] - lo_key;
+        }
+        mode = kCand;
+        continue;  // the loop head's barrier publishes aux
+      }
+      // a radix pass over the bracket
+      prefix |= (uint32_t)found[0] << s2;
+      pmask |= dmask << s2;
+      krem -= found[1];
+      top = s2 - 1;
+      if (top < 0) break;
     }
-    tau = lo + prefix;
+    tau = lo_key + prefix;
     need_eq = krem;
-    __syncthreads();  // cand is reused for the output below
   }
   const int n_sel = min(k, n_valid);
 
-  // ---- slots in position order: scan of packed (gt, eq) counts ----
-  int c4[kTkSeg / 4];
+  // ---- slots in position order ----
+  // Per round, lane counts packed as (gt << 16) | eq (each at most 4 per lane,
+  // 256 per wave); a DPP scan gives the lanes below and the wave's total.
   int wtot = 0;
+  #pragma unroll 1
+  for (int i = 0; i < kTkRounds; ++i) {
+    const uint4 q = keys4[wbase4 + lane + 64 * i];
+    const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+    int c = 0;
 #pragma unroll
-  for (int i = 0; i < kTkSeg / 4; ++i) {
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = kr[4 * i + e];
-      gt += key > tau;
-      eq += (key == tau) & (key != 0u);
-    }
-    c4[i] = (gt << 16) | eq;  // gt <= k <= 4096 and eq <= 32768 per row
-    wtot += c4[i];
+    for (int e = 0; e < 4; ++e) c += ((kk[e] > tau) << 16) | ((kk[e] == tau) & (kk[e] != 0u));
+    wtot += wave_total(c);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wtot += __shfl_xor(wtot, o);
-  __syncthreads();  // every thread has read red (counts above)
-  if (lane == 0) red[wave] = wtot;
+  __syncthreads();  // every thread has read red; aux (candidates) is free
+  if (lane == 0) red[wave] = wtot;  // gt <= 4096 and eq <= 32768 per row
   __syncthreads();
   int run = 0;  // packed counts of the waves before this one
   for (int w = 0; w < wave; ++w) run += red[w];
-  uint32_t* opos = cand;             // [k] virtual positions, in order
-  uint32_t* okey = cand + kTopkMaxK;  // [k] their keys (chunk launches)
+  #pragma unroll 1
+  for (int i = 0; i < kTkRounds; ++i) {
+    const int u = wbase4 + lane + 64 * i;
+    const uint4 q = keys4[u];
+    const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+    int c = 0;
 #pragma unroll
-  for (int i = 0; i < kTkSeg / 4; ++i) {
-    int x = c4[i];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    int before = run + x - c4[i];
-    run += __shfl(x, 63);
-    if (c4[i]) {
+    for (int e = 0; e < 4; ++e) c += ((kk[e] > tau) << 16) | ((kk[e] == tau) & (kk[e] != 0u));
+    const int incl = wave_scan_incl(c);
+    const int before = run + incl - c;
+    run += __builtin_amdgcn_readlane(incl, 63);
+    if (c) {
       int gtb = before >> 16, eqb = before & 0xffff;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = kr[4 * i + e];
-        const bool g = key > tau, q = (key == tau) & (key != 0u);
-        if (g || (q && eqb < need_eq)) {
-          const int slot = gtb + min(eqb, need_eq);
-          opos[slot] = (uint32_t)(wbase + 4 * (lane + 64 * i) + e);
-          if (out_score) okey[slot] = key;
-        }
+        const bool g = kk[e] > tau, eq = (kk[e] == tau) & (kk[e] != 0u);
+        if (g || (eq && eqb < need_eq)) aux[gtb + min(eqb, need_eq)] = (uint32_t)(4 * u + e);
         gtb += g;
-        eqb += q;
+        eqb += eq;
       }
     }
   }
   __syncthreads();
   for (int i = tid; i < k; i += kTkThreads) {
     if (i < n_sel) {
-      const int v = (int)opos[i];
+      const int v = min((int)aux[i], n - 1);  // (a slot is always < n)
       out_idx[i] = vpos ? vpos[v] : pos_base + v;
-      if (out_score) out_score[i] = key_score(okey[i]);
+      if (out_score) out_score[i] = key_score(keys[v]);
     } else {
       out_idx[i] = -1;
       if (out_score) out_score[i] = -INFINITY;
@@ -372,8 +521,7 @@ static int topk_chunks(int L) { return (L + kTkRow - 1) / kTkRow; }
 bool topk_supported(int L, int k) {
   if (k < 1 || k > kTopkMaxK) return false;
   const int nch = topk_chunks(L);
-  // many rows take the one-work-group-per-row kernel, whose merge of long
-  // rows holds ceil(L/32768) * k candidates
+  // the merge launch holds ceil(L / 32768) * k candidates in one work-group
   return nch == 1 || (int64_t)nch * k <= kTkRow;
 }
 
