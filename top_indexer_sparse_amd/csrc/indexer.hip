@@ -183,10 +183,20 @@ struct QueryRegs {
 };
 
 // One query per grid row; waves split the positions of the work-group.  Each
-// wave streams a contiguous range through a ring of kDecRing key chunks, so
-// kDecRing - 1 chunks (12 KB of bf16 keys per wave) stay in flight while one
-// is consumed.
-constexpr int kDecRing = 4;
+// wave streams a contiguous range through a register ring of R key chunks
+// (16 positions each), so R - 1 chunks (28 KB of bf16 keys per wave at R = 8)
+// stay in flight while one is consumed; R shrinks to 4 where the query block
+// alone takes half the registers (H^I x d^I = 128 x 128).  The loop body is free of conditional memory operations: ring
+// loads are always issued (rows past the range are clamped to its last valid
+// row and their scores ignored), and scores go to a per-wave LDS buffer, so
+// the compiler's vmcnt waits count exactly the older chunk's loads instead of
+// draining the ring.  The scores (times the fp8 scale) leave with coalesced
+// stores after the loop.
+constexpr int kDecMaxRing = 8;
+constexpr int kDecMaxSpan = 1024;                    // positions per wave, at most
+constexpr int kDecBuf = kDecMaxSpan + 16 * kDecMaxRing;  // + the ring's overrun
+template <int HT, int DI>
+constexpr int dec_ring() { return 16 * HT * DI >= 16384 ? 4 : kDecMaxRing; }
 
 template <int HT, int DI, bool FP8>
 __global__ __launch_bounds__(256) void idx_decode_kernel(
@@ -196,6 +206,9 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
     int T, int L, int s_per_wave, float* __restrict__ scores) {
   constexpr int HI = 16 * HT;
   constexpr int ROWB = FP8 ? DI : 2 * DI;  // bytes per key row
+  constexpr int NSC = kDecMaxSpan / 64;    // prefetched scales per lane
+  constexpr int R = dec_ring<HT, DI>();
+  __shared__ float sbuf[4][kDecBuf];
   const int64_t bt = blockIdx.y;
   const int b = (int)(bt / T);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -211,30 +224,46 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   if (s_begin >= v_end) return;
 
   const uint8_t* kb = k + (int64_t)b * L * ROWB;
-  const float* scb = kscale ? kscale + (int64_t)b * L : nullptr;
   const int nch = (v_end - s_begin + 15) / 16;
   auto row_of = [&](int c) { return kb + (int64_t)min(s_begin + 16 * c + n, v_end - 1) * ROWB; };
 
-  KeyChunk<DI, FP8> ring[kDecRing];
-#pragma unroll
-  for (int i = 0; i < kDecRing; ++i)
-    if (i < nch) ring[i].load(row_of(i), g);
   QueryRegs<HT, DI, FP8> qr;
   qr.load(q + bt * HI * DI, w + bt * HI, lane);
-
-  for (int c0 = 0; c0 < nch; c0 += kDecRing) {
+  // The query and weights must have landed before the ring starts: loads
+  // still pending at the loop entry would make every iteration's vmcnt wait
+  // count the ring's own loads and drain it.
+  wait_vmcnt<0>();
+  float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
+  if constexpr (FP8) {
+    const float* scb = kscale + (int64_t)b * L;
 #pragma unroll
-    for (int i = 0; i < kDecRing; ++i) {
+    for (int i = 0; i < NSC; ++i)
+      scr[i] = scb[min(s_begin + lane + 64 * i, v_end - 1)];
+  }
+  // The ring is filled by the loop itself (its first pass only loads), so the
+  // ring registers are the same on every pass and at the loop entry.
+  KeyChunk<DI, FP8> ring[R];
+  float* sb = sbuf[wave];
+  for (int c0 = -R; c0 < nch; c0 += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
       const int c = c0 + i;
-      if (c < nch) {
-        float sc = qr.score(ring[i]);
-        if (c + kDecRing < nch) ring[i].load(row_of(c + kDecRing), g);
-        const int s = s_begin + 16 * c + n;
-        if (g == 0 && s < v_end) {
-          if (scb) sc *= scb[s];
-          out[s] = sc;
-        }
+      if (c0 >= 0) {  // uniform; chunks past nch are computed and dropped
+        const float sc = qr.score(ring[i]);
+        sb[16 * c + n] = sc;  // the four lane groups write the same value
       }
+      ring[i].load(row_of(c + R), g);
+    }
+  }
+  // the wave's own LDS writes are ordered before these reads
+  const int span = v_end - s_begin;
+#pragma unroll
+  for (int i = 0; i < NSC; ++i) {
+    const int j = lane + 64 * i;
+    if (j < span) {
+      float v = sb[j];
+      if constexpr (FP8) v *= scr[i];
+      out[s_begin + j] = v;
     }
   }
 }
@@ -354,7 +383,7 @@ static hipError_t launch_mfma(const IndexerArgs& a, hipStream_t st) {
   } else {
     // long per-wave ranges amortise the query registers; shrink them only
     // until the grid has ~2 waves per SIMD (512 work-groups of 4 waves)
-    int s_per_wave = 1024;
+    int s_per_wave = kDecMaxSpan;
     const int64_t rows = (int64_t)a.B * a.T;
     while (s_per_wave > 64 && rows * ((a.L + 4 * s_per_wave - 1) / (4 * s_per_wave)) < 512)
       s_per_wave /= 2;
