@@ -19,7 +19,8 @@ The JSON line carries, besides the contract fields:
                 indexer source changed since they were taken;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--steps K] [--warmup W]
+       [--workload decode_32k|decode_128k_fp8|prefill_16k]
        [--no-cpu-baseline] [--kernel-only]
 """
 import argparse
@@ -128,31 +129,36 @@ def measured_traffic():
     return round(fetch + write)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_32k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-only", action="store_true",
-                    help="only the fused steps (for profiler runs)")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="also run 3 plain device copies of MIB MiB (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(decode shards by sequence, with no exchange between GPUs). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def timed_after(step, fn, n, stream):
+    """Mean duration of fn, each launch timed alone with HIP events on
+    `stream` right after an untimed step (so caches hold what they hold
+    inside the step loop)."""
     import torch
-    from top_indexer_sparse_amd import api
-    api.load()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        step()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / n
 
+
+def copy_probe(mib, dev):
+    import torch
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 x {mib} MiB device copies")
+
+
+def run_decode(args, api, dev):
+    import torch
     log(f"generating {args.workload}")
     wl = make_workload(args.workload)
     t = wl.to(dev)
@@ -186,43 +192,41 @@ def main():
     log(f"{ms * 1e3:.1f} us/step, {qps:,.0f} queries/s, whole step {100 * step_frac:.1f}% "
         f"of HBM peak ({wall:.2f} s wall)")
     if args.copy_probe:
-        src = torch.empty(args.copy_probe << 18, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy probe: 3 x {args.copy_probe} MiB device copies")
+        copy_probe(args.copy_probe, dev)
     if args.kernel_only:
-        return
+        return None
 
-    # dominant kernel: the indexer, one launch at a time on the same stream,
-    # each right after an untimed fused step, so that caches hold what they
-    # hold inside the step loop (the 256 MB Infinity Cache does not keep the
-    # 268 MB of keys between steps; back-to-back indexer launches would see
-    # partial hits)
+    # the indexer (the metric's HBM-bound stage) and the sparse MLA, each
+    # timed launch by launch after an untimed fused step
     scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
+    mout = torch.empty_like(out)
+    mlse = torch.empty_like(lse)
+    mws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_MLA_FORWARD, B, 1, L, k,
+                                                              wl.H, wl.dc)),
+                      dtype=torch.uint8, device=dev)
 
     def idx_only():
         api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, k_scale=t.k_scale,
                                        kv_len=t.kv_len, scores=scores, stream=stream)
 
+    def mla_only():
+        api.sparse_attn_mla_forward(t.q_lat, t.q_rope, c_kv, k_rope, idx, wl.sm_scale,
+                                    out=mout, lse=mlse, ws=mws, stream=stream)
+
     idx_only()
+    mla_only()
     n_roof = max(5, min(args.steps, 50))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_roof)]
-    torch.cuda.synchronize()
-    for e0, e1 in ev:
-        step()
-        e0.record(stream)
-        idx_only()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    idx_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / n_roof
+    idx_ms = timed_after(step, idx_only, n_roof, stream)
+    mla_ms = timed_after(step, mla_only, n_roof, stream)
     idx_bytes = B * (ki + qi)
     idx_gbs = idx_bytes / (idx_ms * 1e-3) / 1e9
+    mla_bytes = B * (gather + qm + o)
+    mla_flop = B * 2 * wl.H * k * ((wl.dc + wl.dR) + wl.dc)
+    mla_tfs = mla_flop / (mla_ms * 1e-3) / 1e12
     log(f"indexer {idx_ms * 1e3:.1f} us/launch (each after a step), "
         f"{idx_gbs:,.0f} GB/s algorithmic")
+    log(f"sparse MLA {mla_ms * 1e3:.1f} us/launch incl. split combine, "
+        f"{mla_tfs:,.0f} TFLOP/s, {mla_bytes / (mla_ms * 1e-3) / 1e9:,.0f} GB/s")
 
     result = {
         "metric": "decode queries/s at L=32K,k=2048; indexer+gather % of HBM roofline",
@@ -248,11 +252,148 @@ def main():
                      "traffic": measured_traffic() if args.workload == "decode_32k" else None,
                      "launch_us": round(idx_ms * 1e3, 2),
                      "bytes_per_launch": idx_bytes},
+        "roofline_mla": {"bound": "mfma", "kernel": "sparse MLA + split combine",
+                         "achieved": round(mla_tfs, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(mla_tfs / BF16_PEAK_TFLOPS, 4),
+                         "hbm_frac": round(mla_bytes / (mla_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "launch_us": round(mla_ms * 1e3, 2), "flop_per_launch": mla_flop,
+                         "bytes_per_launch": mla_bytes},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a sample")
         result["cpu_baseline"] = cpu_baseline(wl)
-    print(json.dumps(result), flush=True)
+    return result
+
+
+def prefill_indexer_flop(wl):
+    """2 H^I d^I flop per (query t, candidate s <= t), over the causal triangle."""
+    pairs = wl.T * (wl.T + 1) // 2
+    return pairs * 2 * wl.HI * wl.dI
+
+
+def run_prefill(args, api, dev):
+    """Causal prefill, T = L = 16384: indexer (MFMA contraction with the causal
+    mask) -> top-k per query row -> sparse MLA for every query."""
+    import torch
+    from top_indexer_sparse_amd import workloads
+    log("generating prefill_16k")
+    wl = workloads.prefill_16k()
+    t = wl.to(dev)
+    T, L, k = wl.T, wl.L, wl.topk
+    c_kv, k_rope = t.kv[..., :wl.dc], t.kv[..., wl.dc:]
+    scores = torch.empty((1, T, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, T), dtype=torch.int32, device=dev)
+    out = torch.empty((1, T, wl.H, wl.dc), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, T, wl.H), dtype=torch.float32, device=dev)
+    tws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_TOPK, 1, T, L, k, 0, 0)),
+                      dtype=torch.uint8, device=dev)
+    mws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_MLA_FORWARD, 1, T, L, k,
+                                                              wl.H, wl.dc)),
+                      dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def indexer():
+        api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, q_pos=t.q_pos, scores=scores,
+                                       stream=stream)
+
+    def step():
+        indexer()
+        api.sparse_attn_topk(scores, k, q_pos=t.q_pos, idx=idx, count=cnt, ws=tws,
+                             stream=stream)
+        api.sparse_attn_mla_forward(t.q_lat, t.q_rope, c_kv, k_rope, idx, wl.sm_scale,
+                                    out=out, lse=lse, ws=mws, stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms = time_events(step, args.steps, stream)
+    qps = T / (ms * 1e-3)
+    log(f"{ms:.2f} ms/step, {qps:,.0f} queries/s")
+    if args.kernel_only:
+        return None
+    idx_ms = timed_after(step, indexer, max(3, min(args.steps, 10)), stream)
+    flop = prefill_indexer_flop(wl)
+    tfs = flop / (idx_ms * 1e-3) / 1e12
+    log(f"indexer {idx_ms:.3f} ms, {tfs:,.0f} TFLOP/s = {100 * tfs / BF16_PEAK_TFLOPS:.1f}% "
+        f"of bf16 MFMA peak")
+    result = {
+        "metric": "prefill queries/s at T=L=16K, k=2048; indexer % of bf16 MFMA peak",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": 1, "T": T, "L": L, "topk": k, "HI": wl.HI,
+                   "dI": wl.dI, "H": wl.H, "dc": wl.dc, "dR": wl.dR},
+        "roofline": {"bound": "mfma", "kernel": "indexer (causal QK^T)", "achieved": round(tfs, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "launch_us": round(idx_ms * 1e3, 1), "flop_per_launch": flop},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on a sample")
+        result["cpu_baseline"] = cpu_baseline_prefill(wl)
+    return result
+
+
+def cpu_baseline_prefill(wl, stride=64):
+    """The oracle on every `stride`-th query row of the prefill (full causal
+    rows, top-k and sparse MLA), in queries/s."""
+    import oracle
+    import torch
+    rows = torch.arange(stride - 1, wl.T, stride)
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    s = oracle.indexer(wl.q_idx[:, rows], wl.w[:, rows], wl.k_idx, q_pos=wl.q_pos[:, rows])
+    idx, _ = oracle.topk(s, wl.topk, q_pos=wl.q_pos[:, rows])
+    oracle.sparse_mla(wl.q_lat[:, rows], wl.q_rope[:, rows], wl.kv, idx, wl.sm_scale, dc=wl.dc)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "queries/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"every {stride}th query row of prefill_16k ({len(rows)} rows, causal "
+                      f"L up to {wl.L}), fp64 C oracle on {threads} threads, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_32k",
+                    choices=["decode_32k", "decode_128k_fp8", "prefill_16k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only the timed steps (for profiler runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run 3 plain device copies of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(decode shards by sequence, with no exchange between GPUs). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from top_indexer_sparse_amd import api
+    api.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == "prefill_16k":
+        result = run_prefill(args, api, dev)
+    else:
+        result = run_decode(args, api, dev)
+    if result is not None:
+        print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -194,72 +194,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
 #pragma unroll
   for (int d4 = 0; d4 < 4; ++d4) voff[d4] = 16 * ((2 * d4 + ((n & 3) >> 1)) ^ mv) + 8 * (n & 1);
 
-  for (int tl = 0; tl < ntiles; ++tl) {
-    // this wave's part of tile tl landed (loads return in order; the tiles
-    // issued after it may still be in flight)
-    const int ahead = min(kMlaBuf - 2, ntiles - 1 - tl);
-    if (ahead >= 2)
-      wait_vmcnt<2 * NLD>();
-    else if (ahead == 1)
-      wait_vmcnt<NLD>();
-    else
-      wait_vmcnt<0>();
-    wait_lgkm0();
-    lds_barrier();  // every wave's part landed; tile tl-1 no longer read
-    if (tl + kMlaBuf - 1 < ntiles) issue(tl + kMlaBuf - 1);
-    const uint8_t* tb = tiles[tl % kMlaBuf];
-
-    // S^T[jt]: rows 16 jt + 4 g + r, head n.  The two row blocks are two
-    // independent accumulator chains, interleaved, with the K operands of the
-    // next k-step loaded while the current one multiplies.
-    floatx4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint8_t* r0 = tb + n * kMlaRowB;
-      const uint8_t* r1 = r0 + 16 * kMlaRowB;
-      auto kop = [&](const uint8_t* rp, int ks) {
-        return *(const uintx4*)(rp + 128 * (ks >> 1) + ((ks & 1) ? qoff1 : qoff0));
-      };
-      uintx4 a0 = kop(r0, 0), a1 = kop(r1, 0);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        uintx4 b0, b1;
-        if (ks + 1 < 18) {
-          b0 = kop(r0, ks + 1);
-          b1 = kop(r1, ks + 1);
-        }
-        st0 = mfma16x16x32(as_bf16x8(a0), qb[ks], st0);
-        st1 = mfma16x16x32(as_bf16x8(a1), qb[ks], st1);
-        if (ks + 1 < 18) {
-          a0 = b0;
-          a1 = b1;
-        }
-      }
-    }
-    // scale to log2 units, mask skipped slots, tile max per head
-    float x[8];
-    float mt = -INFINITY;
-    const uint32_t vm = svmask[tl] >> (4 * g);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v0 = (vm >> r) & 1u ? st0[r] * a.scale_log2 : -INFINITY;
-      const float v1 = (vm >> (16 + r)) & 1u ? st1[r] * a.scale_log2 : -INFINITY;
-      x[r] = v0;
-      x[4 + r] = v1;
-      mt = fmaxf(mt, fmaxf(v0, v1));
-    }
-    mt = max_over_lane_groups(mt);
-    // Lazy rescaling: the reference max m_run moves only when a score exceeds
-    // it by more than 8 (log2 units), so the weights exp2(x - m_run) stay below
-    // 256 and the fp32 accumulators are rescaled only on such jumps.
-    const bool grow = mt > m_run + 8.f;
-    if (__ballot(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // 0 at first
-      if (grow) m_run = mt;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  // P = exp2(x - m_use) as bf16 hi + lo, and O^T += V^T P^T for tile tb.
+  auto pv_step = [&](const uint8_t* tb, const float (&x)[8], float m_use) {
     // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits, so
     // the product stays at fp32-level accuracy while the MFMAs stay bf16.
     uint32_t pbh[4], pbl[4];
@@ -310,6 +246,108 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
         va = na;
         vb = nb;
       }
+    }
+    // schedule: the first two d-tiles' transpose reads, then per d-tile pair
+    // the next pair's four reads (while any remain) and its four products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int dt = 0; dt < 32; dt += 2) {
+      if (dt + 2 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    }
+  };
+
+  // The tile loop touches O only through MFMAs, so the accumulators stay in
+  // AGPRs.  A wave leaves it when a score of the current tile exceeds its
+  // reference max by more than 8 (log2 units; always at the first tile): the
+  // rescale O *= 2^(m_old - m_new) runs outside the loop, finishes that tile
+  // and re-enters.  Weights exp2(x - m_run) therefore stay below 256.
+  int tl = 0;
+  float x[8];
+  float mt = -INFINITY;
+  const uint8_t* tb = tiles[0];
+  for (;;) {
+    bool rescale = false;
+  for (; tl < ntiles; ++tl) {
+    // this wave's part of tile tl landed (loads return in order; the tiles
+    // issued after it may still be in flight)
+    const int ahead = min(kMlaBuf - 2, ntiles - 1 - tl);
+    if (ahead >= 2)
+      wait_vmcnt<2 * NLD>();
+    else if (ahead == 1)
+      wait_vmcnt<NLD>();
+    else
+      wait_vmcnt<0>();
+    wait_lgkm0();
+    lds_barrier();  // every wave's part landed; tile tl-1 no longer read
+    if (tl + kMlaBuf - 1 < ntiles) issue(tl + kMlaBuf - 1);
+    tb = tiles[tl % kMlaBuf];
+
+    // S^T[jt]: rows 16 jt + 4 g + r, head n.  The two row blocks are two
+    // independent accumulator chains, interleaved, with the K operands of the
+    // next k-step loaded while the current one multiplies.
+    floatx4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* r0 = tb + n * kMlaRowB;
+      const uint8_t* r1 = r0 + 16 * kMlaRowB;
+      auto kop = [&](const uint8_t* rp, int ks) {
+        return *(const uintx4*)(rp + 128 * (ks >> 1) + ((ks & 1) ? qoff1 : qoff0));
+      };
+      // K operands run kQkAhead k-steps ahead of the products that use them,
+      // enough to cover the LDS latency with one wave per SIMD.
+      constexpr int kQkAhead = 3;
+      uintx4 k0[kQkAhead + 1], k1[kQkAhead + 1];
+#pragma unroll
+      for (int i = 0; i < kQkAhead; ++i) {
+        k0[i] = kop(r0, i);
+        k1[i] = kop(r1, i);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks + kQkAhead < 18) {
+          k0[(ks + kQkAhead) % (kQkAhead + 1)] = kop(r0, ks + kQkAhead);
+          k1[(ks + kQkAhead) % (kQkAhead + 1)] = kop(r1, ks + kQkAhead);
+        }
+        st0 = mfma16x16x32(as_bf16x8(k0[ks % (kQkAhead + 1)]), qb[ks], st0);
+        st1 = mfma16x16x32(as_bf16x8(k1[ks % (kQkAhead + 1)]), qb[ks], st1);
+      }
+      // keep that order in the schedule: the first 2 kQkAhead reads, then per
+      // k-step two reads (while any remain) and its two products
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks + kQkAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    }
+    // scale to log2 units, mask skipped slots, tile max per head
+    mt = -INFINITY;
+    const uint32_t vm = svmask[tl] >> (4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v0 = (vm >> r) & 1u ? st0[r] * a.scale_log2 : -INFINITY;
+      const float v1 = (vm >> (16 + r)) & 1u ? st1[r] * a.scale_log2 : -INFINITY;
+      x[r] = v0;
+      x[4 + r] = v1;
+      mt = fmaxf(mt, fmaxf(v0, v1));
+    }
+    mt = max_over_lane_groups(mt);
+    if (__ballot(mt > m_run + 8.f)) {
+      rescale = true;
+      break;
+    }
+    pv_step(tb, x, m_run == -INFINITY ? 0.f : m_run);
+  }
+    if (!rescale) break;
+    {
+      const bool grow = mt > m_run + 8.f;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // 0 at first
+      if (grow) m_run = mt;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) o[i] *= alpha;
+      pv_step(tb, x, m_run == -INFINITY ? 0.f : m_run);
+      ++tl;
     }
   }
 
