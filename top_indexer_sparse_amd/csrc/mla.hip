@@ -103,21 +103,48 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   const int nslots = max(0, min(a.k, j_begin + a.slots_per_split) - j_begin);
   const int32_t* idxr = a.idx + bt * a.k + j_begin;
 
+  // Q^T operand: qb[ks] = q[h][32 ks + 8 g .. +8], ks < 16 from q_lat, 16..17
+  // q_rope.  Issued first, so it arrives while the index slice is processed.
+  bf16x8 qb[18];
+  {
+    const uint16_t* ql = a.q_lat + (bt * a.H + h) * (int64_t)kMlaDc;
+    const uint16_t* qr = a.q_rope + (bt * a.H + h) * (int64_t)kMlaDr;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(*(const uintx4*)(ql + 32 * ks + 8 * g));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qb[16 + ks] = as_bf16x8(*(const uintx4*)(qr + 32 * ks + 8 * g));
+  }
+
   // ---- the split's index slice -> LDS; skipped slots fetch a valid row ----
+  // One round of loads (up to kMlaMaxSplitSlots / (64 NW) slots per thread,
+  // all in flight together), one LDS minimum for the first valid position,
+  // then the position table and the per-tile validity masks.
+  constexpr int kSlotsPerThread = kMlaMaxSplitSlots / (64 * NW);
+  int sv[kSlotsPerThread];
+#pragma unroll
+  for (int i = 0; i < kSlotsPerThread; ++i) {
+    const int j = tid + 64 * NW * i;
+    sv[i] = j < nslots ? idxr[j] : -1;
+  }
   if (tid == 0) sfirst = 0x7fffffff;
   __syncthreads();
-  for (int j = tid; j < nslots; j += 64 * NW) {
-    const int s = idxr[j];
-    if (s >= 0 && s < a.L) atomicMin(&sfirst, s);
+  {
+    int mn = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i)
+      if (sv[i] >= 0 && sv[i] < a.L) mn = min(mn, sv[i]);
+    if (mn != 0x7fffffff) atomicMin(&sfirst, mn);
   }
   __syncthreads();
   const int first = sfirst;
   const int ntiles = first == 0x7fffffff ? 0 : (nslots + kMlaTile - 1) / kMlaTile;
-  for (int j0 = 0; j0 < ntiles * kMlaTile; j0 += 64 * NW) {  // uniform trip count
+#pragma unroll
+  for (int i = 0; i < kSlotsPerThread; ++i) {
+    const int j0 = 64 * NW * i;
+    if (j0 >= ntiles * kMlaTile) break;  // uniform
     const int j = j0 + tid;
-    const int s = j < nslots ? idxr[j] : -1;
-    const bool ok = s >= 0 && s < a.L;
-    if (j < ntiles * kMlaTile) spos[j] = ok ? s : first;
+    const bool ok = sv[i] >= 0 && sv[i] < a.L;
+    if (j < ntiles * kMlaTile) spos[j] = ok ? sv[i] : first;
     const uint64_t m = __ballot(ok);  // 64 slots = two tiles
     if (lane == 0 && j < ntiles * kMlaTile) {
       svmask[j / kMlaTile] = (uint32_t)m;
@@ -150,9 +177,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   auto issue = [&](int tl) {
     const uint32_t dst = lds0 + (uint32_t)((tl % kMlaBuf) * kMlaTileB);
     const uint8_t* sp = (const uint8_t*)spos + 4 * tl * kMlaTile;
+    // every row position first: the DMA asm carries a memory clobber, so a
+    // position read placed after one DMA would wait out a full LDS round trip
+    uint32_t srow[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) srow[i] = *(const uint32_t*)(sp + drow[i]);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const uint32_t s = *(const uint32_t*)(sp + drow[i]);
+      const uint32_t s = srow[i];
       const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NW * i);
       if constexpr (PACKED) {
         dma16(cb, s * (uint32_t)a.c_stride_b + dpiece[i], ldst);
@@ -165,16 +197,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     }
   };
 
-  // Q^T operand: qb[ks] = q[h][32 ks + 8 g .. +8], ks < 16 from q_lat, 16..17 q_rope
-  bf16x8 qb[18];
-  {
-    const uint16_t* ql = a.q_lat + (bt * a.H + h) * (int64_t)kMlaDc;
-    const uint16_t* qr = a.q_rope + (bt * a.H + h) * (int64_t)kMlaDr;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(*(const uintx4*)(ql + 32 * ks + 8 * g));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qb[16 + ks] = as_bf16x8(*(const uintx4*)(qr + 32 * ks + 8 * g));
-  }
   wait_vmcnt<0>();  // Q is in registers before the tile loads start counting
 #pragma unroll
   for (int t = 0; t < kMlaBuf - 1; ++t)
