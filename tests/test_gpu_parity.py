@@ -287,6 +287,34 @@ def test_staged_path_equals_fused_decode():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def test_fused_decode_ragged_batch():
+    """Fused decode over B=10 sequences with ragged kv_len (down to one valid
+    position): index sets equal the staged path's, outputs match the oracle,
+    and work queued right after it on the caller's stream sees the result."""
+    _announce("fused decode: B=10 L=4100 ragged kv_len")
+    B, L = 10, 4100
+    kv_len = [4100, 4000, 3000, 2100, 2048, 2047, 100, 4100, 1, 3333]
+    wl = workloads.decode_32k(B=B, L=L, kv_len=kv_len)
+    t = wl.to(DEV)
+    c_kv, k_rope = t.kv[..., :wl.dc], t.kv[..., wl.dc:]
+    s = api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, kv_len=t.kv_len)
+    idx, cnt = api.sparse_attn_topk(s, wl.topk, kv_len=t.kv_len)
+    out2, lse2, idx2 = api.sparse_attn_decode(t.q_idx, t.w, t.k_idx, None, t.kv_len, wl.topk,
+                                              t.q_lat, t.q_rope, c_kv, k_rope, wl.sm_scale)
+    # consume on the caller's stream right away: ordering is the library's job
+    total = out2.abs().sum() + lse2.nan_to_num(neginf=0.0).abs().sum()
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.isfinite(total).item()
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, idx2.cpu().numpy(), wl.sm_scale,
+                               dc=wl.dc)
+    assert_attention_close(out2, ro, ATTN_ATOL_BF16, lse2, rl)
+    rs = oracle.indexer(wl.q_idx, wl.w, wl.k_idx, kv_len=wl.kv_len)
+    oi, oc = oracle.topk(rs, wl.topk, kv_len=wl.kv_len)
+    gi = idx2.cpu().numpy()
+    assert_index_sets(gi, (gi >= 0).sum(-1), oi, oc, rs)
+
+
 def test_prefill_path_small_causal():
     _announce("prefill path L=200 H=64")
     L = 200

@@ -83,6 +83,20 @@ __device__ __forceinline__ float max_over_lane_groups(float v) {
   return v;
 }
 
+// The same maximum through gfx950's v_permlane16_swap / v_permlane32_swap
+// (VALU lane exchanges, no LDS round trip).  With both operands equal, the
+// swap hands every lane the pair {v[l], v[l ^ 16]} (then {.., v[l ^ 32]}) in
+// its two results, so max(r0, r1) is the pair maximum in every lane.  Needs
+// all 64 lanes active.
+__device__ __forceinline__ float max_over_lane_groups_vx(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  u = __builtin_bit_cast(uint32_t, v);
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)t[0]), __builtin_bit_cast(float, (uint32_t)t[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;

@@ -32,6 +32,8 @@
 //
 // mla_vector_kernel: fp32 vector ALU, any dc <= 512, dR <= 64, for fp32
 // inputs (and bf16 outside the MFMA shape); one work-group per query.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -174,16 +176,21 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     drow[i] = 4 * r;                  // byte offset into a tile's slice of spos
     dpiece[i] = 16 * (pp ^ row_swz(r));
   }
-  auto issue = [&](int tl) {
+  // Loads I0 <= i < I1 of this wave's share of tile tl.  A tile's loads are
+  // issued in three parts spread over the previous tile's compute: the CU's
+  // address unit takes one 1 KB load per ~16 cycles, so the four waves'
+  // 36 loads issued back to back would stall every wave for ~600 cycles.
+  auto issue_part = [&](int tl, auto I0c, auto I1c) {
+    constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
     const uint32_t dst = lds0 + (uint32_t)((tl % kMlaBuf) * kMlaTileB);
     const uint8_t* sp = (const uint8_t*)spos + 4 * tl * kMlaTile;
     // every row position first: the DMA asm carries a memory clobber, so a
     // position read placed after one DMA would wait out a full LDS round trip
     uint32_t srow[NLD];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) srow[i] = *(const uint32_t*)(sp + drow[i]);
+    for (int i = I0; i < I1; ++i) srow[i] = *(const uint32_t*)(sp + drow[i]);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
+    for (int i = I0; i < I1; ++i) {
       const uint32_t s = srow[i];
       const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NW * i);
       if constexpr (PACKED) {
@@ -196,6 +203,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
       }
     }
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, NLD / 3>;
+  using P2 = std::integral_constant<int, 2 * NLD / 3>;
+  using P3 = std::integral_constant<int, NLD>;
+  auto issue = [&](int tl) { issue_part(tl, P0{}, P3{}); };
 
   wait_vmcnt<0>();  // Q is in registers before the tile loads start counting
 #pragma unroll
@@ -302,7 +314,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
       wait_vmcnt<0>();
     wait_lgkm0();
     lds_barrier();  // every wave's part landed; tile tl-1 no longer read
-    if (tl + kMlaBuf - 1 < ntiles) issue(tl + kMlaBuf - 1);
+    const bool more = tl + kMlaBuf - 1 < ntiles;  // a tile left to fetch
+    if (more) issue_part(tl + kMlaBuf - 1, P0{}, P1{});
     tb = tiles[tl % kMlaBuf];
 
     // S^T[jt]: rows 16 jt + 4 g + r, head n.  The two row blocks are two
@@ -342,6 +355,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
+    if (more) issue_part(tl + kMlaBuf - 1, P1{}, P2{});
     // scale to log2 units, mask skipped slots, tile max per head
     mt = -INFINITY;
     const uint32_t vm = svmask[tl] >> (4 * g);
@@ -353,12 +367,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
       x[4 + r] = v1;
       mt = fmaxf(mt, fmaxf(v0, v1));
     }
-    mt = max_over_lane_groups(mt);
+    mt = max_over_lane_groups_vx(mt);
     if (__ballot(mt > m_run + 8.f)) {
       rescale = true;
       break;
     }
     pv_step(tb, x, m_run == -INFINITY ? 0.f : m_run);
+    if (more) issue_part(tl + kMlaBuf - 1, P2{}, P3{});
   }
     if (!rescale) break;
     {
@@ -369,6 +384,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) o[i] *= alpha;
       pv_step(tb, x, m_run == -INFINITY ? 0.f : m_run);
+      if (tl + kMlaBuf - 1 < ntiles) issue_part(tl + kMlaBuf - 1, P2{}, P3{});
       ++tl;
     }
   }
