@@ -97,6 +97,22 @@ __device__ __forceinline__ float max_over_lane_groups_vx(float v) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)t[0]), __builtin_bit_cast(float, (uint32_t)t[1]));
 }
 
+// Sum over the four lanes {l, l^16, l^32, l^48} by the same lane exchanges.
+// The result is pinned (empty asm) where it is computed, so the compiler
+// cannot sink the exchanges into a divergent branch that uses the sum: with
+// lanes switched off they would read stale values.  Needs all 64 lanes
+// active at the call.
+__device__ __forceinline__ float sum_over_lane_groups_vx(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  u = __builtin_bit_cast(uint32_t, v);
+  auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (uint32_t)t[0]) + __builtin_bit_cast(float, (uint32_t)t[1]);
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;

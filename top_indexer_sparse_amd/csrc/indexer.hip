@@ -178,7 +178,7 @@ struct QueryRegs {
 #pragma unroll
       for (int r = 0; r < 4; ++r) part = fmaf(wr[ht][r], fmaxf(acc[r], 0.f), part);
     }
-    return sum_over_lane_groups(part);
+    return sum_over_lane_groups_vx(part);  // callers run it with the whole wave
   }
 };
 
