@@ -20,7 +20,7 @@ The JSON line carries, besides the contract fields:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W]
-       [--workload decode_32k|decode_128k_fp8|prefill_16k]
+       [--workload decode_32k|decode_128k_fp8|prefill_16k|block_sparse_64k]
        [--no-cpu-baseline] [--kernel-only]
 """
 import argparse
@@ -363,13 +363,116 @@ def cpu_baseline_prefill(wl, stride=64):
                       f"L up to {wl.L}), fp64 C oracle on {threads} threads, {dt:.2f} s"}
 
 
+def block_union_bytes(wl, blocks):
+    """K and V bytes one step must read at least: per (sequence, KV head), the
+    union over its query heads of the visible tokens (chosen blocks, sinks,
+    window), each token's key and value row once."""
+    import numpy as np
+    bl = blocks.cpu().numpy()
+    G = wl.Hq // wl.Hkv
+    row = 2 * wl.d * 2  # key + value, bf16
+    total = 0
+    base = np.zeros(wl.L, dtype=bool)
+    base[:min(wl.n_sink, wl.L)] = True
+    base[max(0, wl.L - wl.n_win):] = True
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            vis = base.copy()
+            for n in bl[b, g * G:(g + 1) * G].reshape(-1):
+                if n >= 0:
+                    vis[n * wl.blk:(n + 1) * wl.blk] = True
+            total += int(vis.sum()) * row
+    return total
+
+
+def run_block(args, api, dev):
+    """Block-sparse GQA decode, B=16, L=65536, 32 query / 8 KV heads: a step is
+    block choice + attention over the visible set, on pooled keys that are
+    built once beforehand (a cache-maintenance step, timed on its own)."""
+    import torch
+    from top_indexer_sparse_amd import workloads
+    log("generating block_sparse_64k")
+    wl = workloads.block_sparse_64k()
+    t = wl.to(dev)
+    stream = torch.cuda.current_stream()
+    krep = torch.empty((wl.B, wl.L // wl.blk, wl.Hkv, wl.d), dtype=torch.float32, device=dev)
+    out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    blocks = torch.empty((wl.B, wl.Hq, wl.nsel), dtype=torch.int32, device=dev)
+    ws = torch.empty(api.sparse_attn_workspace_bytes(api.SA_OP_BLOCK_DECODE, wl.B, wl.Hq, wl.L,
+                                                     wl.nsel, wl.Hkv, wl.d),
+                     dtype=torch.uint8, device=dev)
+
+    def pool():
+        api.sparse_attn_block_pool(t.k, wl.blk, krep=krep, stream=stream)
+
+    def step():
+        api.sparse_attn_block_decode(t.q, t.k, t.v, krep, wl.blk, wl.nsel, wl.n_sink, wl.n_win,
+                                     wl.sm_scale, out=out, blocks_out=blocks, ws=ws,
+                                     stream=stream)
+
+    pool()
+    pool_ms = time_events(pool, 3, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms = time_events(step, args.steps, stream)
+    qps = wl.B / (ms * 1e-3)
+    kv_bytes = block_union_bytes(wl, blocks)
+    krep_bytes = krep.numel() * 4
+    io_bytes = wl.B * wl.Hq * wl.d * (2 + 4)
+    step_bytes = kv_bytes + krep_bytes + io_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"{ms * 1e3:.1f} us/step, {qps:,.0f} queries/s; {step_bytes / 1e6:.1f} MB/step "
+        f"= {gbs:,.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak); "
+        f"pooling {pool_ms * 1e3:.0f} us")
+    result = {
+        "metric": "block-sparse decode queries/s at L=64K, top-16 blocks of 64 + 64 sinks + "
+                  "512 window, GQA 32/8",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "d": wl.d, "blk": wl.blk, "nsel": wl.nsel, "n_sink": wl.n_sink,
+                   "n_win": wl.n_win},
+        "roofline": {"bound": "hbm", "kernel": "block choice + attention (whole step)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": step_bytes},
+        "block_pool_us": round(pool_ms * 1e3, 1),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.num_threads()
+        t0 = time.perf_counter()
+        n = 2
+        for b in range(n):
+            oracle.block_sparse_decode(wl.q[b:b + 1], wl.k[b:b + 1], wl.v[b:b + 1], wl.blk,
+                                       wl.nsel, wl.n_sink, wl.n_win, wl.sm_scale)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(n / dt, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.B} sequences of block_sparse_64k (full L, all 32 heads, "
+                      f"pooling included), fp64 C oracle on {threads} threads, {dt:.2f} s"}
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_32k",
-                    choices=["decode_32k", "decode_128k_fp8", "prefill_16k"])
+                    choices=["decode_32k", "decode_128k_fp8", "prefill_16k",
+                             "block_sparse_64k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the timed steps (for profiler runs)")
@@ -390,6 +493,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "prefill_16k":
         result = run_prefill(args, api, dev)
+    elif args.workload == "block_sparse_64k":
+        result = run_block(args, api, dev)
     else:
         result = run_decode(args, api, dev)
     if result is not None:
