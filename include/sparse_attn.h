@@ -202,8 +202,7 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w,
  * Compiled set: d = 128, blk in {32, 64, 128}, Hq / Hkv in {1, 2, 4, 8},
  * 1 <= nsel <= 64, L / blk <= 8192.
  * ws: sparse_attn_workspace_bytes(SA_OP_BLOCK_DECODE, B, Hq, L, nsel, Hkv, d)
- *   (block scores [B, Hq, L/blk] f32 and the chosen blocks; the query assumes
- *   the smallest block, 32, so it covers every compiled block size).
+ *   (the chosen blocks, [B, Hq, nsel] int32).
  * Errors as for the other entry points; a query head whose visible set is
  * empty (L < blk, no sinks, no window) gets out = 0.
  * ------------------------------------------------------------------------- */

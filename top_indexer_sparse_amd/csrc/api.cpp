@@ -230,7 +230,7 @@ size_t sparse_attn_workspace_bytes(int op, int B, int T, int L, int k, int H, in
     case SA_OP_DECODE:
       return decode_ws(B, L, k, H, dc, SA_BF16).total;
     case SA_OP_BLOCK_DECODE:  // (B, Hq, L, nsel, Hkv, d) passed as (B, T, L, k, H, dc)
-      return sa::block_workspace_bytes(B, T, L, k, H, dc, 32);  // blk >= 32: upper bound
+      return sa::block_workspace_bytes(B, T, L, k, H, dc, 32);
   }
   return 0;
 }

@@ -15,12 +15,11 @@
 //  * block_pool_kernel: one work-group per (block, sequence); 8-byte bf16
 //    loads, fp32 sums.  A cache-maintenance step (the pooled keys of a block
 //    change only when the block fills), not part of a decode step.
-//  * block_select_kernel: one work-group per (KV head, sequence).  The pooled
-//    keys of the KV head are read once and scored against all query heads of
-//    the group (block scores to the workspace); then, head by head, a bitonic
-//    sort of (score key, inverted block index) pairs in LDS puts the best
-//    blocks first with ties to the lower index, and the chosen blocks are
-//    written in ascending order.
+//  * block_select_kernel: one work-group per (query head, sequence).  Block
+//    scores as (score key, inverted block index) keys, so that one maximum
+//    search orders by score with ties to the lower block; the nsel largest by
+//    repeated wave maxima (per wave, then over the four waves' survivors),
+//    written in ascending block order.
 //  * block_attn_kernel: one work-group per (query head, sequence).  The
 //    visible ranges (sinks, chosen blocks, window) are merged into disjoint
 //    ascending ranges; the four waves take 64-token chunks in turn: lane =
@@ -45,14 +44,13 @@ bool block_supported(const BlockArgs& a) {
          a.L / a.blk <= kBlkMaxBlocks;
 }
 
-// scores [B, Hq, nblk] f32 | chosen blocks [B, Hq, nsel] int32
+// chosen blocks [B, Hq, nsel] int32
 size_t block_workspace_bytes(int B, int Hq, int L, int nsel, int Hkv, int d, int blk) {
   (void)Hkv;
   (void)d;
-  if (blk < 1 || B < 0 || Hq < 1 || nsel < 1 || L < 0) return 0;
-  const size_t nblk = (size_t)(L / blk);
-  const size_t sc = ((size_t)B * Hq * nblk * sizeof(float) + 255) & ~(size_t)255;
-  return sc + (size_t)B * Hq * nsel * sizeof(int32_t);
+  (void)L;
+  if (blk < 1 || B < 0 || Hq < 1 || nsel < 1) return 0;
+  return (size_t)B * Hq * nsel * sizeof(int32_t);
 }
 
 // ---------------------------------------------------------------------------
@@ -94,95 +92,122 @@ struct BlockSelArgs {
   const uint16_t* q;    // [B, Hq, d]
   const float* krep;    // [B, nblk, Hkv, d]
   int Hq, Hkv, nblk, nsel;
-  float* scores;        // [B, Hq, nblk]
   int32_t* chosen;      // [B, Hq, nsel] (workspace)
   int32_t* blocks_out;  // [B, Hq, nsel] or null
 };
 
-__global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
-  __shared__ float qs[kBlkMaxGroup][kBlkD];
-  __shared__ uint64_t keys[kBlkMaxBlocks];
-  __shared__ int pick[kBlkMaxSel];
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int G = a.Hq / a.Hkv, h0 = g * G, nblk = a.nblk;
-  for (int i = tid; i < G * kBlkD; i += 256)
-    qs[i / kBlkD][i % kBlkD] = bf16_bits_to_float(a.q[((int64_t)b * a.Hq + h0) * kBlkD + i]);
-  __syncthreads();
-
-  // block scores of every head of the group; thread t takes blocks t, t+256..
-  for (int n = tid; n < nblk; n += 256) {
-    const float4* kr = (const float4*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD);
-    float acc[kBlkMaxGroup];
-#pragma unroll
-    for (int j = 0; j < kBlkMaxGroup; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kBlkD / 32; ++c) {  // 8 x 16 bytes in flight per step
-      float4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = kr[8 * c + i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d0 = 32 * c + 4 * i;
-#pragma unroll
-        for (int j = 0; j < kBlkMaxGroup; ++j) {
-          if (j < G) {
-            acc[j] = fmaf(v[i].x, qs[j][d0], acc[j]);
-            acc[j] = fmaf(v[i].y, qs[j][d0 + 1], acc[j]);
-            acc[j] = fmaf(v[i].z, qs[j][d0 + 2], acc[j]);
-            acc[j] = fmaf(v[i].w, qs[j][d0 + 3], acc[j]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kBlkMaxGroup; ++j)
-      if (j < G) a.scores[((int64_t)b * a.Hq + h0 + j) * nblk + n] = acc[j];
+// Largest 64-bit key over the wave (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), o) << 32) |
+                       (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+    v = w > v ? w : v;
   }
-  // (each thread reads back below exactly the scores it wrote: same stride)
+  return v;
+}
 
-  const int N = nblk > 1 ? 1 << (32 - __clz(nblk - 1)) : 1;  // power of two >= nblk
-  const int m = min(nblk, a.nsel);
-  for (int j = 0; j < G; ++j) {
-    const int h = h0 + j;
-    const float* sc = a.scores + ((int64_t)b * a.Hq + h) * nblk;
-    // (score key, ~block): descending order puts higher scores first and,
-    // among equal scores, the lower block first; padding sorts last
-    for (int i = tid; i < N; i += 256)
-      keys[i] = i < nblk ? ((uint64_t)blk_score_key(sc[i]) << 32) | (uint32_t)~(uint32_t)i : 0ull;
-    __syncthreads();
-    for (int kk = 2; kk <= N; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < N; i += 256) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const uint64_t x = keys[i], y = keys[ixj];
-            const bool desc = (i & kk) == 0;
-            if (desc ? x < y : x > y) {
-              keys[i] = y;
-              keys[ixj] = x;
-            }
-          }
+constexpr int kSelPerLane = kBlkMaxBlocks / 256;  // blocks per thread
+
+// One work-group per (query head, sequence).  Keys (score key << 32 | ~block)
+// order blocks by score, ties to the lower block, so the selection is a
+// plain maximum search: each wave takes the nsel largest keys of its share
+// (nsel rounds of a wave maximum, the winner's lane retiring it), one wave
+// then takes the nsel largest of the 4 nsel survivors the same way.
+__global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
+  __shared__ uint64_t cand[4][kBlkMaxSel];
+  __shared__ int pick[kBlkMaxSel];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = lane_id(), wave = tid >> 6;
+  const int g = h / (a.Hq / a.Hkv), nblk = a.nblk;
+  float qf[kBlkD];
+  {
+    const uint4* qp = (const uint4*)(a.q + ((int64_t)b * a.Hq + h) * kBlkD);
+#pragma unroll
+    for (int i = 0; i < kBlkD / 8; ++i) {
+      const uint4 u = qp[i];
+      qf[8 * i + 0] = bf16_lo(u.x);
+      qf[8 * i + 1] = bf16_hi(u.x);
+      qf[8 * i + 2] = bf16_lo(u.y);
+      qf[8 * i + 3] = bf16_hi(u.y);
+      qf[8 * i + 4] = bf16_lo(u.z);
+      qf[8 * i + 5] = bf16_hi(u.z);
+      qf[8 * i + 6] = bf16_lo(u.w);
+      qf[8 * i + 7] = bf16_hi(u.w);
+    }
+  }
+  // block n = tid + 256 r: one pooled-key row (512 bytes) per lane
+  uint64_t key[kSelPerLane];
+#pragma unroll
+  for (int r = 0; r < kSelPerLane; ++r) {
+    const int n = tid + 256 * r;
+    key[r] = 0ull;
+    if (256 * r >= nblk) continue;  // uniform: nothing left for any thread
+    if (n < nblk) {
+      const float4* kr = (const float4*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD);
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {  // 16 x 16 bytes in flight
+        float4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = kr[16 * c + i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d0 = 64 * c + 4 * i;
+          acc = fmaf(v[i].x, qf[d0], acc);
+          acc = fmaf(v[i].y, qf[d0 + 1], acc);
+          acc = fmaf(v[i].z, qf[d0 + 2], acc);
+          acc = fmaf(v[i].w, qf[d0 + 3], acc);
         }
-        __syncthreads();
       }
+      key[r] = ((uint64_t)blk_score_key(acc) << 32) | (uint32_t)~(uint32_t)n;
     }
-    // the m chosen blocks in ascending order (rank by counting, m <= 64)
-    if (tid < m) pick[tid] = (int)~(uint32_t)keys[tid];
-    __syncthreads();
-    int32_t* ch = a.chosen + ((int64_t)b * a.Hq + h) * a.nsel;
-    int32_t* bo = a.blocks_out ? a.blocks_out + ((int64_t)b * a.Hq + h) * a.nsel : nullptr;
-    if (tid < a.nsel) {
-      int val = -1, rank = tid;
-      if (tid < m) {
-        const int mine = pick[tid];
-        rank = 0;
-        for (int i = 0; i < m; ++i) rank += pick[i] < mine;
-        val = mine;
-      }
-      ch[rank] = val;
-      if (bo) bo[rank] = val;
+  }
+  // this wave's nsel largest keys
+  const int m = min(nblk, a.nsel);
+  for (int i = 0; i < m; ++i) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int r = 0; r < kSelPerLane; ++r) best = key[r] > best ? key[r] : best;
+    const uint64_t w = wave_max_u64(best);
+    if (lane == 0) cand[wave][i] = w;
+    if (w != 0ull) {  // the owner retires the winning key (keys are distinct)
+#pragma unroll
+      for (int r = 0; r < kSelPerLane; ++r) key[r] = key[r] == w ? 0ull : key[r];
     }
-    __syncthreads();  // keys / pick are reused by the next head
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // the nsel largest of the 4 m survivors: lane l holds candidates l, l+64..
+    uint64_t c4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = lane + 64 * r;  // candidate j = (wave j / m, rank j % m)
+      c4[r] = j < 4 * m ? cand[j / m][j % m] : 0ull;
+    }
+    for (int i = 0; i < m; ++i) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) best = c4[r] > best ? c4[r] : best;
+      const uint64_t w = wave_max_u64(best);
+      if (lane == 0) pick[i] = (int)~(uint32_t)w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c4[r] = c4[r] == w ? 0ull : c4[r];
+    }
+  }
+  __syncthreads();
+  // ascending order: rank of each chosen block among the chosen (m <= 64)
+  int32_t* ch = a.chosen + ((int64_t)b * a.Hq + h) * a.nsel;
+  int32_t* bo = a.blocks_out ? a.blocks_out + ((int64_t)b * a.Hq + h) * a.nsel : nullptr;
+  if (tid < a.nsel) {
+    int val = -1, rank = tid;
+    if (tid < m) {
+      const int mine = pick[tid];
+      rank = 0;
+      for (int i = 0; i < m; ++i) rank += pick[i] < mine;
+      val = mine;
+    }
+    ch[rank] = val;
+    if (bo) bo[rank] = val;
   }
 }
 
@@ -392,8 +417,6 @@ hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d, int bl
 hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int nblk = a.L / a.blk;
-  char* ws = (char*)a.ws;
-  const size_t sc_bytes = ((size_t)a.B * a.Hq * nblk * sizeof(float) + 255) & ~(size_t)255;
   BlockSelArgs s{};
   s.q = (const uint16_t*)a.q;
   s.krep = a.krep;
@@ -401,10 +424,9 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   s.Hkv = a.Hkv;
   s.nblk = nblk;
   s.nsel = a.nsel;
-  s.scores = (float*)ws;
-  s.chosen = (int32_t*)(ws + sc_bytes);
+  s.chosen = (int32_t*)a.ws;
   s.blocks_out = a.blocks_out;
-  block_select_kernel<<<dim3(a.Hkv, a.B), 256, 0, st>>>(s);
+  block_select_kernel<<<dim3(a.Hq, a.B), 256, 0, st>>>(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   BlockAttnArgs t{};
