@@ -274,7 +274,7 @@ constexpr int kPfWaves = 8;
 constexpr int kPfTile = 64;
 
 template <int HT, int DI, bool FP8>
-__global__ __launch_bounds__(512) void idx_prefill_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(HT <= 4 ? 4 : 2))) void idx_prefill_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ k, const float* __restrict__ kscale,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kv_len,
