@@ -154,6 +154,14 @@ __device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint32
                : "s"(lds_base), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+// A wave-uniform pointer, moved to SGPRs (for the SGPR base of the copies).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 // Work-group barrier without the memory fence of __syncthreads (which would
 // also wait for the tiles still in flight); "memory" keeps the compiler from

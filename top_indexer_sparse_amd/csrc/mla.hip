@@ -8,11 +8,10 @@
 // 数学学习笔记" §2, §8, §9).  All heads of a query read the same rows.
 //
 // mla_mfma_kernel (bf16, dc = 512, dR = 64): a work-group is four waves of 16
-// heads each and walks a range of the query's slots 32 rows at a time.  The
-// 32 gathered rows (1152 bytes each: 1024 of c_kv, 128 of k_rope) arrive in
-// LDS by direct global->LDS loads (global_load_lds_dwordx4), four tile
-// buffers deep, so three tiles (108 KB) are in flight while one is consumed:
-// random row gathers are latency-bound and need that depth.  Per wave and
+// heads each (one wave per SIMD) and walks a range of the query's slots 32
+// rows at a time.  The 32 gathered rows (1152 bytes each: 1024 of c_kv, 128
+// of k_rope) arrive in LDS by direct global->LDS copies
+// (global_load_lds_dwordx4) into a ring of four tile buffers.  Per wave and
 // tile:
 //   S^T[32 rows x 16 heads] = K[32 x 576] Q^T            (36 MFMA 16x16x32)
 //   online softmax per head (each lane owns one head: a lane's S^T values all
@@ -25,8 +24,16 @@
 // through ds_read_b64_tr_b16, which hands each lane four consecutive rows of
 // one column.  P enters the product as two bf16 terms, P_hi = bf16(P) and
 // P_lo = bf16(P - P_hi) (two MFMAs on the same V^T operand, so no extra LDS
-// traffic); a single bf16 P would perturb each weight by up to 2^-9, which
+// traffic); a single bf16 P would perturb each weight by up to 2^-8, which
 // breaks a 2e-3 max-abs bound when few rows carry the mass.
+// The tile loop is software-pipelined: step t computes S(t), then the
+// previous tile's PV products with the softmax of S(t) issued between them;
+// tiles t and t-1 are in use, t+1 and t+2 in flight.  At one wave per SIMD
+// the loop is bound by LDS operand reads (each wave reads every K and V row
+// of the tile), so K and V operands are fetched several MFMA steps ahead.
+// The prologue also moves everything through global->LDS copies with explicit
+// waits (index slice, then the queries, staged in two tile buffers), so the
+// first tiles are requested while the queries are still arriving.
 // Long index sets are split over work-groups (KV split); a combine kernel
 // merges the partial (m, l, o) by log-sum-exp.
 //
@@ -38,6 +45,15 @@
 #include "launch.hpp"
 
 namespace sa {
+
+// f(integral_constant<I>) for I = B .. E-1, in order, at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA path
@@ -75,19 +91,23 @@ struct MlaKernelArgs {
   float* part_ml;          // [BT, H, nsplit, 2]
 };
 
-// NW waves of 16 heads each; one work-group per (query, head group, KV split).
+// NW waves; one work-group per (query, head group, KV split).  Each wave owns
+// 16 heads and 512 / DS of the output dims: with DS = 2, the two waves of a
+// pair compute the same scores and softmax and split the value product, which
+// halves the accumulators and lets two waves share a SIMD.
 // PACKED: k_rope row = c_kv row + 1024 bytes with one stride ([B, L, 576]).
-template <int NW, bool PACKED>
+template <int NW, bool PACKED, int DS>
 __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kMlaBuf][kMlaTileB];
   __shared__ int spos[kMlaMaxSplitSlots];                  // row to fetch (always valid)
   __shared__ uint32_t svmask[kMlaMaxSplitSlots / kMlaTile];  // bit r: row r counts
-  __shared__ int sfirst;
 
   // block -> (bt, head group, split); blocks that share (bt, split) are placed
   // on the same XCD (blocks are dealt to the 8 XCDs round-robin) so the head
   // groups' re-reads of the gathered rows hit that XCD's L2.
-  constexpr int HW = 16 * NW;
+  constexpr int NH = NW / DS;  // head blocks of 16 per work-group
+  constexpr int HW = 16 * NH;
+  constexpr int ND = 32 / DS;  // d-tiles of 16 output dims per wave
   const int hgroups = a.H / HW;
   const int nblk = gridDim.x;
   int lin = blockIdx.x;
@@ -99,79 +119,73 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int h = hg * HW + wave * 16 + n;  // this lane's head
+  const int hb = wave % NH, dh = wave / NH;  // head block, output-dim part
+  const int h = hg * HW + hb * 16 + n;       // this lane's head
 
   const int j_begin = split * a.slots_per_split;
   const int nslots = max(0, min(a.k, j_begin + a.slots_per_split) - j_begin);
   const int32_t* idxr = a.idx + bt * a.k + j_begin;
 
-  // Q^T operand: qb[ks] = q[h][32 ks + 8 g .. +8], ks < 16 from q_lat, 16..17
-  // q_rope.  Issued first, so it arrives while the index slice is processed.
-  bf16x8 qb[18];
-  {
-    const uint16_t* ql = a.q_lat + (bt * a.H + h) * (int64_t)kMlaDc;
-    const uint16_t* qr = a.q_rope + (bt * a.H + h) * (int64_t)kMlaDr;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(*(const uintx4*)(ql + 32 * ks + 8 * g));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qb[16 + ks] = as_bf16x8(*(const uintx4*)(qr + 32 * ks + 8 * g));
-  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tiles[0][0];
+  const uint32_t lds_spos = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&spos[0];
 
-  // ---- the split's index slice -> LDS; skipped slots fetch a valid row ----
-  // One round of loads (up to kMlaMaxSplitSlots / (64 NW) slots per thread,
-  // all in flight together), one LDS minimum for the first valid position,
-  // then the position table and the per-tile validity masks.
-  constexpr int kSlotsPerThread = kMlaMaxSplitSlots / (64 * NW);
-  int sv[kSlotsPerThread];
-#pragma unroll
-  for (int i = 0; i < kSlotsPerThread; ++i) {
-    const int j = tid + 64 * NW * i;
-    sv[i] = j < nslots ? idxr[j] : -1;
-  }
-  if (tid == 0) sfirst = 0x7fffffff;
-  __syncthreads();
+  // ---- prologue: every load is a global->LDS copy with an explicit wait ----
+  // (the compiler tracks none of them, so no wait of its own drains the tile
+  // copies issued later).  First the split's index slice into spos (slot j at
+  // spos[j]; slots past the slice read a clamped in-row address and are
+  // masked below), then the work-group's queries into tile buffers 2
+  // and 3, laid out per (head block, k-step) as 1 KB runs in the MFMA B
+  // operand order, so that the register loads below are conflict-free.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave index in an SGPR
   {
-    int mn = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kSlotsPerThread; ++i)
-      if (sv[i] >= 0 && sv[i] < a.L) mn = min(mn, sv[i]);
-    if (mn != 0x7fffffff) atomicMin(&sfirst, mn);
-  }
-  __syncthreads();
-  const int first = sfirst;
-  const int ntiles = first == 0x7fffffff ? 0 : (nslots + kMlaTile - 1) / kMlaTile;
-#pragma unroll
-  for (int i = 0; i < kSlotsPerThread; ++i) {
-    const int j0 = 64 * NW * i;
-    if (j0 >= ntiles * kMlaTile) break;  // uniform
-    const int j = j0 + tid;
-    const bool ok = sv[i] >= 0 && sv[i] < a.L;
-    if (j < ntiles * kMlaTile) spos[j] = ok ? sv[i] : first;
-    const uint64_t m = __ballot(ok);  // 64 slots = two tiles
-    if (lane == 0 && j < ntiles * kMlaTile) {
-      svmask[j / kMlaTile] = (uint32_t)m;
-      if (j / kMlaTile + 1 < ntiles) svmask[j / kMlaTile + 1] = (uint32_t)(m >> 32);
+    const uint8_t* ib = uniform_ptr((const uint8_t*)(a.idx + bt * a.k));
+    const int nrun = (nslots + 63) / 64;
+    for (int r = wu; r < nrun; r += NW) {
+      const int j = min(j_begin + 64 * r + lane, a.k - 1);
+      dma4(ib, 4u * (uint32_t)j, lds_spos + 256u * (uint32_t)r);
     }
   }
-  __syncthreads();
+  static_assert(kMlaBuf >= 4 && NH * 18 % NW == 0, "query staging layout");
+  constexpr int kQRuns = NH * 18 / NW;  // 1 KB query runs per wave
+  {
+    const uint8_t* qlb = uniform_ptr((const uint8_t*)(a.q_lat + (bt * a.H + (int64_t)hg * HW) * kMlaDc));
+    const uint8_t* qrb = uniform_ptr((const uint8_t*)(a.q_rope + (bt * a.H + (int64_t)hg * HW) * kMlaDr));
+    const int qn = lane >> 2, qg = lane & 3;
+#pragma unroll
+    for (int i = 0; i < kQRuns; ++i) {
+      const int q = wu + NW * i;  // run q = (head block q / 18, k-step q % 18)
+      const int qhb = q / 18, ks = q % 18;
+      const uint32_t head = (uint32_t)(16 * qhb + qn);
+      const uint32_t dst = lds0 + 2u * kMlaTileB + 1024u * (uint32_t)q;
+      if (ks < 16)
+        dma16(qlb, head * (2u * kMlaDc) + 64u * ks + 16u * qg, dst);
+      else
+        dma16(qrb, head * (2u * kMlaDr) + 64u * (ks - 16) + 16u * qg, dst);
+    }
+  }
+  wait_vmcnt<kQRuns>();  // this wave's index slice landed (the query runs may not)
+  lds_barrier();         // every wave's slice landed
+  // Every slot of the slice is processed; a slot that holds no position in
+  // [0, L) fetches row 0 and is masked out of the softmax.
+  const int ntiles = (nslots + kMlaTile - 1) / kMlaTile;
 
-  // ---- tile fetch: wave w issues the 1 KB pieces q = w, w + NW, ... ----
+  // ---- tile fetch: wave w < NH issues the 1 KB pieces q = w, w + NH, ... ----
   // Lane l of load i fills 16-byte slot c = 64 q + l of the tile: row c / 72,
   // position c % 72, which holds piece (c % 72) ^ swz(row).  Rows and pieces
   // are the same for every tile, so they are computed once; per load only the
   // gathered row's position changes.  The packed layout (k_rope right after
   // c_kv in one row, as a [B, L, 576] cache) needs one base and one stride; a
   // split cache takes the piece's own base.
-  static_assert(kMlaTileLoads % NW == 0, "equal loads per wave");
-  constexpr int NLD = kMlaTileLoads / NW;  // loads per tile and wave
+  static_assert(kMlaTileLoads % NH == 0, "equal loads per wave");
+  constexpr int NLD = kMlaTileLoads / NH;  // loads per tile and issuing wave
   const uint8_t* cb = a.c_kv + (int64_t)b * a.L * a.c_stride_b;
   const uint8_t* rb = a.k_rope + (int64_t)b * a.L * a.r_stride_b;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tiles[0][0];
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = __builtin_amdgcn_readfirstlane(hb);
+  const bool issuer = __builtin_amdgcn_readfirstlane(dh) == 0;
   uint32_t drow[NLD], dpiece[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int c = 64 * (wv + NW * i) + lane;
+    const int c = 64 * (wv + NH * i) + lane;
     const int r = c / kMlaPieces, pp = c % kMlaPieces;
     drow[i] = 4 * r;                  // byte offset into a tile's slice of spos
     dpiece[i] = 16 * (pp ^ row_swz(r));
@@ -182,6 +196,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   // 36 loads issued back to back would stall every wave for ~600 cycles.
   auto issue_part = [&](int tl, auto I0c, auto I1c) {
     constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
+    if (!issuer) return;
     const uint32_t dst = lds0 + (uint32_t)((tl % kMlaBuf) * kMlaTileB);
     const uint8_t* sp = (const uint8_t*)spos + 4 * tl * kMlaTile;
     // every row position first: the DMA asm carries a memory clobber, so a
@@ -191,8 +206,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     for (int i = I0; i < I1; ++i) srow[i] = *(const uint32_t*)(sp + drow[i]);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-      const uint32_t s = srow[i];
-      const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NW * i);
+      const uint32_t s = srow[i] < (uint32_t)a.L ? srow[i] : 0u;  // skipped slot: row 0
+      const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NH * i);
       if constexpr (PACKED) {
         dma16(cb, s * (uint32_t)a.c_stride_b + dpiece[i], ldst);
       } else {
@@ -209,14 +224,53 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   using P3 = std::integral_constant<int, NLD>;
   auto issue = [&](int tl) { issue_part(tl, P0{}, P3{}); };
 
-  wait_vmcnt<0>();  // Q is in registers before the tile loads start counting
+  // Tiles 0 and 1 go out now, behind the query runs; tile t + 2 is issued
+  // while tile t is consumed.
 #pragma unroll
-  for (int t = 0; t < kMlaBuf - 1; ++t)
+  for (int t = 0; t < 2; ++t)
     if (t < ntiles) issue(t);
-
-  floatx4 o[32];
+  // per-tile validity masks (bit r: slot 32 t + r holds a position in [0, L))
+  constexpr int kSlotsPerThread = kMlaMaxSplitSlots / (64 * NW);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kSlotsPerThread; ++i) {
+    const int j0 = 64 * NW * i;
+    if (j0 >= ntiles * kMlaTile) break;  // uniform
+    const int j = j0 + tid;
+    const bool ok = j < nslots && (uint32_t)spos[j] < (uint32_t)a.L;
+    const uint64_t m = __ballot(ok);  // 64 slots = two tiles
+    const int t0 = j0 / kMlaTile + 2 * wave;  // this wave's first tile
+    if (lane == 0 && t0 < ntiles) {
+      svmask[t0] = (uint32_t)m;
+      if (t0 + 1 < ntiles) svmask[t0 + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  // the query runs landed (they precede the tile copies); Q^T operand
+  // qb[ks] = q[h][32 ks + 8 g .. +8], ks < 16 from q_lat, 16..17 from q_rope
+  if (issuer && ntiles >= 2)
+    wait_vmcnt<2 * NLD>();
+  else if (issuer && ntiles == 1)
+    wait_vmcnt<NLD>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  bf16x8 qb[18];
+  {
+    const uint8_t* qs = &tiles[2][0] + 18 * 1024 * hb + 16 * (4 * n + g);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qb[ks] = as_bf16x8(*(const uintx4*)(qs + 1024 * ks));
+  }
+  wait_lgkm0();
+  lds_barrier();  // buffers 2 and 3 are free again
+  // The step before the first multiplies a zero P by buffer 3: clear it so
+  // that no stale LDS bits (a NaN pattern) reach the accumulators.
+  {
+    uintx4* zb = (uintx4*)tiles[kMlaBuf - 1];
+    for (int i = tid; i < kMlaTileB / 16; i += 64 * NW) zb[i] = uintx4{0u, 0u, 0u, 0u};
+  }
+
+  floatx4 o[ND];  // d-tile ND dh + i
+#pragma unroll
+  for (int i = 0; i < ND; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   // per-lane byte offsets of the swizzled reads
@@ -228,11 +282,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
 #pragma unroll
   for (int d4 = 0; d4 < 4; ++d4) voff[d4] = 16 * ((2 * d4 + ((n & 3) >> 1)) ^ mv) + 8 * (n & 1);
 
-  // P = exp2(x - m_use) as bf16 hi + lo, and O^T += V^T P^T for tile tb.
-  auto pv_step = [&](const uint8_t* tb, const float (&x)[8], float m_use) {
-    // P = P_hi + P_lo, both bf16: the pair carries ~16 significant bits, so
-    // the product stays at fp32-level accuracy while the MFMAs stay bf16.
-    uint32_t pbh[4], pbl[4];
+  // P = exp2(x - m_use) as bf16 hi + lo; returns the row sum of P.  The pair
+  // carries ~16 significant bits, so the product stays at fp32-level accuracy
+  // while the MFMAs stay bf16.
+  auto make_p = [&](const float (&x)[8], float m_use, uint32_t (&ph)[4], uint32_t (&pl)[4]) {
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -240,17 +293,25 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
       const float p1 = __builtin_amdgcn_exp2f(x[e + 1] - m_use);
       psum += p0 + p1;
       const uint32_t hi = pack_bf16x2_rne(p0, p1);
-      pbh[e / 2] = hi;
-      pbl[e / 2] = pack_bf16x2_rne(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
+      ph[e / 2] = hi;
+      pl[e / 2] = pack_bf16x2_rne(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
     }
-    l_run += psum;
-    const bf16x8 pBh = __builtin_bit_cast(bf16x8, uintx4{pbh[0], pbh[1], pbh[2], pbh[3]});
-    const bf16x8 pBl = __builtin_bit_cast(bf16x8, uintx4{pbl[0], pbl[1], pbl[2], pbl[3]});
-    // V^T operand: rows R..R+3 -> lane group g, column 16 dt + lane%16 (see the
-    // transpose-read note in common.hpp); piece 2 dt + (lane%4)/2, half lane%2.
-    // Operands of d-tile dt+1 load while dt multiplies; the hi and lo products
-    // of one accumulator are separated by the other d-tile's product.
-    const uint8_t* v0 = tb + R * kMlaRowB;
+    return psum;
+  };
+
+  // O^T += V^T P^T for the tile in tb.  V^T operand: rows R..R+3 -> lane group
+  // g, column 16 dt + lane%16 (see the transpose-read note in common.hpp);
+  // piece 2 dt + (lane%4)/2, half lane%2.  The wave's ND d-tiles go in
+  // chunks of two: a chunk loads the next chunk's operands, multiplies its own (the hi
+  // and lo products of one accumulator separated by the other d-tile's
+  // product) and then runs piece(chunk), a slice of other VALU work; a
+  // scheduling barrier closes each chunk, so that work issues while the
+  // matrix unit runs the chunk's four products.
+  auto pv_mfma = [&](const uint8_t* tb, const uint32_t (&ph)[4], const uint32_t (&pl)[4],
+                     auto&& piece) {
+    const bf16x8 pBh = __builtin_bit_cast(bf16x8, uintx4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 pBl = __builtin_bit_cast(bf16x8, uintx4{pl[0], pl[1], pl[2], pl[3]});
+    const uint8_t* v0 = tb + R * kMlaRowB + 32 * ND * dh;  // the wave's output dims
     const uint8_t* v1 = v0 + 16 * kMlaRowB;
     auto vop = [&](int dt) {
       const int off = 128 * (dt >> 2) + voff[dt & 3];
@@ -264,63 +325,68 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))});
     };
-    bf16x8 va = vop(0), vb = vop(1);
-#pragma unroll
-    for (int dt = 0; dt < 32; dt += 2) {
-      bf16x8 na, nb;
-      if (dt + 2 < 32) {
-        na = vop(dt + 2);
-        nb = vop(dt + 3);
+    // kPvAhead chunks of operands in flight: LDS reads return after a few
+    // hundred cycles when the unit is busy, so one chunk ahead would stall
+    // every chunk on its operands
+    constexpr int kPvAhead = 3;
+    bf16x8 vr[kPvAhead + 1][2];
+    static_for<0, kPvAhead>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      vr[i][0] = vop(2 * i);
+      vr[i][1] = vop(2 * i + 1);
+    });
+    static_for<0, ND / 2>([&](auto kc) {
+      constexpr int c = decltype(kc)::value, dt = 2 * c;
+      if constexpr (c + kPvAhead < ND / 2) {
+        vr[(c + kPvAhead) % (kPvAhead + 1)][0] = vop(2 * (c + kPvAhead));
+        vr[(c + kPvAhead) % (kPvAhead + 1)][1] = vop(2 * (c + kPvAhead) + 1);
       }
+      const bf16x8 va = vr[c % (kPvAhead + 1)][0], vb = vr[c % (kPvAhead + 1)][1];
       o[dt] = mfma16x16x32(va, pBh, o[dt]);
       o[dt + 1] = mfma16x16x32(vb, pBh, o[dt + 1]);
       o[dt] = mfma16x16x32(va, pBl, o[dt]);
       o[dt + 1] = mfma16x16x32(vb, pBl, o[dt + 1]);
-      if (dt + 2 < 32) {
-        va = na;
-        vb = nb;
-      }
-    }
-    // schedule: the first two d-tiles' transpose reads, then per d-tile pair
-    // the next pair's four reads (while any remain) and its four products
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int dt = 0; dt < 32; dt += 2) {
-      if (dt + 2 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-    }
+      piece(kc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
+  auto no_piece = [](auto) {};
 
-  // The tile loop touches O only through MFMAs, so the accumulators stay in
-  // AGPRs.  A wave leaves it when a score of the current tile exceeds its
-  // reference max by more than 8 (log2 units; always at the first tile): the
-  // rescale O *= 2^(m_old - m_new) runs outside the loop, finishes that tile
-  // and re-enters.  Weights exp2(x - m_run) therefore stay below 256.
+  // Software pipeline over the tiles: step t multiplies S(t) = K(t) Q^T, then
+  // runs the previous tile's PV products with the softmax of S(t) placed
+  // between them, so the exponentials and conversions issue while the matrix
+  // unit works.  Tiles t and t-1 are in use during step t; t+1 and t+2 are
+  // in flight.  The accumulators are touched only by MFMAs inside the loop,
+  // so they stay in AGPRs.  A wave leaves the loop when a score of tile t
+  // exceeds its reference max by more than 8 (log2 units; always at the
+  // first tile with a visible row): the rescale O *= 2^(m_old - m_new) runs
+  // outside the loop, after the previous tile's products, redoes P(t) and
+  // re-enters.  Weights exp2(x - m_run) therefore stay below 256.
+  uint32_t pbh[4] = {0u, 0u, 0u, 0u}, pbl[4] = {0u, 0u, 0u, 0u};  // P(t - 1)
   int tl = 0;
   float x[8];
   float mt = -INFINITY;
-  const uint8_t* tb = tiles[0];
   for (;;) {
     bool rescale = false;
   for (; tl < ntiles; ++tl) {
-    // this wave's part of tile tl landed (loads return in order; the tiles
-    // issued after it may still be in flight)
-    const int ahead = min(kMlaBuf - 2, ntiles - 1 - tl);
-    if (ahead >= 2)
-      wait_vmcnt<2 * NLD>();
-    else if (ahead == 1)
+    // this wave's part of tile tl landed (loads return in order; tile tl+1
+    // may still be in flight)
+    if (tl + 1 < ntiles)
       wait_vmcnt<NLD>();
     else
       wait_vmcnt<0>();
     wait_lgkm0();
-    lds_barrier();  // every wave's part landed; tile tl-1 no longer read
-    const bool more = tl + kMlaBuf - 1 < ntiles;  // a tile left to fetch
-    if (more) issue_part(tl + kMlaBuf - 1, P0{}, P1{});
-    tb = tiles[tl % kMlaBuf];
+    lds_barrier();  // every wave's part landed; tile tl-2 no longer read
+    const bool more = tl + 2 < ntiles;  // a tile left to fetch
+    if (more) issue_part(tl + 2, P0{}, P1{});
+    const uint8_t* tb = tiles[tl % kMlaBuf];
+    const uint8_t* tp = tiles[(tl + kMlaBuf - 1) % kMlaBuf];
+    const uint32_t vm = svmask[tl] >> (4 * g);
 
     // S^T[jt]: rows 16 jt + 4 g + r, head n.  The two row blocks are two
-    // independent accumulator chains, interleaved, with the K operands of the
-    // next k-step loaded while the current one multiplies.
+    // independent accumulator chains, interleaved.  K operands run kQkAhead
+    // k-steps ahead of their products; scheduling barriers keep the reads in
+    // k-step order, so the first product waits only for its own operands.
     floatx4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
     {
       const uint8_t* r0 = tb + n * kMlaRowB;
@@ -328,83 +394,105 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
       auto kop = [&](const uint8_t* rp, int ks) {
         return *(const uintx4*)(rp + 128 * (ks >> 1) + ((ks & 1) ? qoff1 : qoff0));
       };
-      // K operands run kQkAhead k-steps ahead of the products that use them,
-      // enough to cover the LDS latency with one wave per SIMD.
-      constexpr int kQkAhead = 3;
+      constexpr int kQkAhead = 5;
       uintx4 k0[kQkAhead + 1], k1[kQkAhead + 1];
-#pragma unroll
-      for (int i = 0; i < kQkAhead; ++i) {
+      static_for<0, kQkAhead>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         k0[i] = kop(r0, i);
         k1[i] = kop(r1, i);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        if (ks + kQkAhead < 18) {
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<0, 18>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + kQkAhead < 18) {
           k0[(ks + kQkAhead) % (kQkAhead + 1)] = kop(r0, ks + kQkAhead);
           k1[(ks + kQkAhead) % (kQkAhead + 1)] = kop(r1, ks + kQkAhead);
         }
         st0 = mfma16x16x32(as_bf16x8(k0[ks % (kQkAhead + 1)]), qb[ks], st0);
         st1 = mfma16x16x32(as_bf16x8(k1[ks % (kQkAhead + 1)]), qb[ks], st1);
-      }
-      // keep that order in the schedule: the first 2 kQkAhead reads, then per
-      // k-step two reads (while any remain) and its two products
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        if (ks + kQkAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
-    if (more) issue_part(tl + kMlaBuf - 1, P1{}, P2{});
-    // scale to log2 units, mask skipped slots, tile max per head
-    mt = -INFINITY;
-    const uint32_t vm = svmask[tl] >> (4 * g);
+    if (more) issue_part(tl + 2, P1{}, P2{});
+
+    // previous tile's PV, with this tile's softmax in pieces between its
+    // products: scale to log2 units and mask skipped slots, tile max per head
+    // (then across the four lane groups), and P against the current
+    // reference max.  P is computed even when the rescale path will redo it.
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+    uint32_t nph[4], npl[4];
+    pv_mfma(tp, pbh, pbl, [&](auto kc) {
+      constexpr int c = decltype(kc)::value;
+      if constexpr (c < 2) {
+        const floatx4& st = c == 0 ? st0 : st1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v0 = (vm >> r) & 1u ? st0[r] * a.scale_log2 : -INFINITY;
-      const float v1 = (vm >> (16 + r)) & 1u ? st1[r] * a.scale_log2 : -INFINITY;
-      x[r] = v0;
-      x[4 + r] = v1;
-      mt = fmaxf(mt, fmaxf(v0, v1));
+        for (int r = 0; r < 4; ++r)
+          x[4 * c + r] = (vm >> (16 * c + r)) & 1u ? st[r] * a.scale_log2 : -INFINITY;
+      } else if constexpr (c == 2) {
+        mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      } else if constexpr (c >= 3 && c < 7) {
+        const int e = 2 * (c - 3);
+        const float p0 = __builtin_amdgcn_exp2f(x[e] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(x[e + 1] - m_use);
+        psum += p0 + p1;
+        const uint32_t hi = pack_bf16x2_rne(p0, p1);
+        nph[e / 2] = hi;
+        npl[e / 2] = pack_bf16x2_rne(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
+      } else if constexpr (c == 7) {
+        mt = max_over_lane_groups_vx(mt);
+      }
+    });
+    // keep P in this block: only the rescale path discards it
+    asm volatile("" ::"v"(nph[0]), "v"(nph[1]), "v"(nph[2]), "v"(nph[3]), "v"(npl[0]),
+                 "v"(npl[1]), "v"(npl[2]), "v"(npl[3]), "v"(psum));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pbh[i] = nph[i];
+      pbl[i] = npl[i];
     }
-    mt = max_over_lane_groups_vx(mt);
+    if (more) issue_part(tl + 2, P2{}, P3{});
     if (__ballot(mt > m_run + 8.f)) {
       rescale = true;
       break;
     }
-    pv_step(tb, x, m_run == -INFINITY ? 0.f : m_run);
-    if (more) issue_part(tl + kMlaBuf - 1, P2{}, P3{});
+    l_run += psum;
   }
     if (!rescale) break;
     {
+      // O holds the products up to tile tl-1; P(tl) is redone against the
+      // new reference max
       const bool grow = mt > m_run + 8.f;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // 0 at first
       if (grow) m_run = mt;
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-      pv_step(tb, x, m_run == -INFINITY ? 0.f : m_run);
-      if (tl + kMlaBuf - 1 < ntiles) issue_part(tl + kMlaBuf - 1, P2{}, P3{});
+      for (int i = 0; i < ND; ++i) o[i] *= alpha;
+      l_run += make_p(x, m_run == -INFINITY ? 0.f : m_run, pbh, pbl);
       ++tl;
     }
   }
-
+  // the last tile's products
+  if (ntiles > 0) {
+    pv_mfma(tiles[(ntiles - 1) % kMlaBuf], pbh, pbl, no_piece);
+  }
   // ---- finish ----
   const float l_tot = sum_over_lane_groups(l_run);
   if (a.nsplit == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* orow = a.out + (bt * a.H + h) * (int64_t)kMlaDc;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *(floatx4*)(orow + 16 * dt + 4 * g) = o[dt] * inv;
-    if (a.lse && g == 0)
+    for (int dt = 0; dt < ND; ++dt)
+      *(floatx4*)(orow + 16 * (ND * dh + dt) + 4 * g) = o[dt] * inv;
+    if (a.lse && g == 0 && dh == 0)
       a.lse[bt * a.H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const int64_t u = (bt * a.H + h) * a.nsplit + split;
     float* orow = a.part_o + u * kMlaDc;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(floatx4*)(orow + 16 * dt + 4 * g) = o[dt];
-    if (g == 0) {
+    for (int dt = 0; dt < ND; ++dt) *(floatx4*)(orow + 16 * (ND * dh + dt) + 4 * g) = o[dt];
+    if (g == 0 && dh == 0) {
       a.part_ml[2 * u] = m_run;
       a.part_ml[2 * u + 1] = l_tot;
     }
@@ -574,8 +662,9 @@ static size_t vector_lds_bytes(int H, int dc, int dR) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-constexpr int kMlaWaves = 4;  // 64 heads per work-group
-constexpr int kMlaHeadsWg = 16 * kMlaWaves;
+constexpr int kMlaWaves = 4;  // one wave per SIMD
+constexpr int kMlaDs = 1;     // each wave computes all 512 output dims of its 16 heads
+constexpr int kMlaHeadsWg = 16 * kMlaWaves / kMlaDs;  // 64
 
 bool mla_uses_mfma(const MlaArgs& a) {
   return a.dtype == SA_BF16 && a.dc == kMlaDc && a.dR == kMlaDr && a.H % kMlaHeadsWg == 0;
@@ -638,9 +727,9 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
     }
     const int64_t nblk = bt * (a.H / kMlaHeadsWg) * m.nsplit;
     if (m.packed)
-      mla_mfma_kernel<kMlaWaves, true><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
+      mla_mfma_kernel<kMlaWaves, true, kMlaDs><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
     else
-      mla_mfma_kernel<kMlaWaves, false><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
+      mla_mfma_kernel<kMlaWaves, false, kMlaDs><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || m.nsplit == 1) return e;
     mla_combine_kernel<<<(unsigned)(bt * a.H), 128, 0, st>>>(m.part_o, m.part_ml, m.nsplit,
