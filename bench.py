@@ -408,7 +408,7 @@ def run_block(args, api, dev):
     def step():
         api.sparse_attn_block_decode(t.q, t.k, t.v, krep, wl.blk, wl.nsel, wl.n_sink, wl.n_win,
                                      wl.sm_scale, out=out, blocks_out=blocks, ws=ws,
-                                     stream=stream)
+                                     stream=stream, shared_choice=args.shared_choice)
 
     pool()
     pool_ms = time_events(pool, 3, stream)
@@ -428,7 +428,8 @@ def run_block(args, api, dev):
         f"pooling {pool_ms * 1e3:.0f} us")
     result = {
         "metric": "block-sparse decode queries/s at L=64K, top-16 blocks of 64 + 64 sinks + "
-                  "512 window, GQA 32/8",
+                  "512 window, GQA 32/8" + (", block choice shared per KV group"
+                                            if args.shared_choice else ""),
         "value": round(qps, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -442,7 +443,7 @@ def run_block(args, api, dev):
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "d": wl.d, "blk": wl.blk, "nsel": wl.nsel, "n_sink": wl.n_sink,
-                   "n_win": wl.n_win},
+                   "n_win": wl.n_win, "shared_choice": bool(args.shared_choice)},
         "roofline": {"bound": "hbm", "kernel": "block choice + attention (whole step)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
@@ -456,7 +457,8 @@ def run_block(args, api, dev):
         n = 2
         for b in range(n):
             oracle.block_sparse_decode(wl.q[b:b + 1], wl.k[b:b + 1], wl.v[b:b + 1], wl.blk,
-                                       wl.nsel, wl.n_sink, wl.n_win, wl.sm_scale)
+                                       wl.nsel, wl.n_sink, wl.n_win, wl.sm_scale,
+                                       shared=args.shared_choice)
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {
             "value": round(n / dt, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
@@ -474,6 +476,9 @@ def main():
                     choices=["decode_32k", "decode_128k_fp8", "prefill_16k",
                              "block_sparse_64k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-choice", action="store_true",
+                    help="block_sparse_64k: one block choice per KV group (sum of its heads' "
+                         "block scores)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the timed steps (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

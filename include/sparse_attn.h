@@ -196,6 +196,10 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w,
  *   lower block index); visible set = those blocks' tokens, union the first
  *   n_sink tokens, union the last n_win tokens; one softmax with sm_scale over
  *   the union (each token once); out[b,h,:] = sum softmax * v[b,j,g,:].
+ *   shared_choice = 1: the query heads of a KV group share one block choice,
+ *   ranked by the sum of the group's block scores, ties to the lower block
+ *   ("MLA 与稀疏注意力" section on choosing blocks and merging outputs, and its
+ *   worked example); 0: each query head chooses by its own scores.
  *   q [B, Hq, d] bf16; k, v [B, L, Hkv, d] bf16; krep from block_pool.
  *   out [B, Hq, d] fp32; blocks_out [B, Hq, nsel] int32 (may be NULL): the
  *   selected block indices in ascending order (-1 when fewer blocks exist).
@@ -212,8 +216,9 @@ int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d,
 int sparse_attn_block_decode(const void* q, const void* k, const void* v,
                              const float* krep, int B, int L, int Hq, int Hkv,
                              int d, int blk, int nsel, int n_sink, int n_win,
-                             float sm_scale, float* out, int32_t* blocks_out,
-                             void* ws, size_t ws_bytes, void* stream);
+                             float sm_scale, int shared_choice, float* out,
+                             int32_t* blocks_out, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------
  * Helpers.

@@ -50,7 +50,7 @@ def lib():
                                      I, D, P, P]
         L.orc_block_pool.argtypes = [P, I, I, I, I, I, P]
         L.orc_block_sparse_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I,
-                                              I, I, D, P, P]
+                                              I, I, D, I, P, P]
         for f in ("orc_indexer", "orc_topk", "orc_sparse_mla", "orc_masked_mla",
                   "orc_block_pool", "orc_block_sparse_decode"):
             getattr(L, f).restype = I
@@ -236,8 +236,12 @@ def block_pool(k, blk):
     return out
 
 
-def block_sparse_decode(q, k, v, blk, nsel, n_sink, n_win, sm_scale, krep=None):
-    """GQA block-sparse decode -> (out[B,Hq,d], blocks[B,Hq,nsel])."""
+def block_sparse_decode(q, k, v, blk, nsel, n_sink, n_win, sm_scale, krep=None,
+                        shared=False):
+    """GQA block-sparse decode -> (out[B,Hq,d], blocks[B,Hq,nsel]).
+
+    shared=True: the query heads of a KV group share one block choice, by the
+    sum of their block scores ("MLA 与稀疏注意力", block choice and merging)."""
     qd, kd, vd = decode(q), decode(k), decode(v)
     B, Hq, d = qd.shape
     L, Hkv = kd.shape[1], kd.shape[2]
@@ -246,6 +250,7 @@ def block_sparse_decode(q, k, v, blk, nsel, n_sink, n_win, sm_scale, krep=None):
     blocks = np.empty((B, Hq, max(nsel, 1)), dtype=np.int32)
     _check(lib().orc_block_sparse_decode(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(kr),
                                          B, L, Hq, Hkv, d, blk, nsel, n_sink,
-                                         n_win, sm_scale, _ptr(out),
-                                         _ptr(blocks)), "block_sparse_decode")
+                                         n_win, sm_scale, int(bool(shared)),
+                                         _ptr(out), _ptr(blocks)),
+           "block_sparse_decode")
     return out, blocks[..., :nsel]

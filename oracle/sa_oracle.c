@@ -342,7 +342,8 @@ int orc_block_pool(const double* k, int B, int L, int Hkv, int d, int blk,
 int orc_block_sparse_decode(const double* q, const double* k, const double* v,
                             const double* krep, int B, int L, int Hq, int Hkv,
                             int d, int blk, int nsel, int n_sink, int n_win,
-                            double sm_scale, double* out, int32_t* blocks_out) {
+                            double sm_scale, int shared, double* out,
+                            int32_t* blocks_out) {
   if (!q || !k || !v || !krep || !out || B < 0 || L < 1 || Hq < 1 ||
       Hkv < 1 || Hq % Hkv || d < 1 || blk < 1 || nsel < 0 || n_sink < 0 ||
       n_win < 0)
@@ -366,12 +367,19 @@ int orc_block_sparse_decode(const double* q, const double* k, const double* v,
       if (!c || !vis || !z || !sel) continue;
       int b = (int)(u / Hq), h = (int)(u % Hq), g = h / group;
       const double* qh = q + u * d;
-      /* block scores against the mean-pooled block keys */
+      /* block scores against the mean-pooled block keys: the head's own, or
+         with `shared` the sum over the heads of its KV group */
+      int h0 = shared ? g * group : h, h1 = shared ? h0 + group : h + 1;
       for (int n = 0; n < nblk; ++n) {
         const double* kr = krep + (((int64_t)b * nblk + n) * Hkv + g) * d;
-        double dot = 0.0;
-        for (int i = 0; i < d; ++i) dot += qh[i] * kr[i];
-        c[n].score = dot;
+        double total = 0.0;
+        for (int hh = h0; hh < h1; ++hh) {
+          const double* qs = q + ((int64_t)b * Hq + hh) * d;
+          double dot = 0.0;
+          for (int i = 0; i < d; ++i) dot += qs[i] * kr[i];
+          total += dot;
+        }
+        c[n].score = total;
         c[n].pos = n;
       }
       qsort(c, (size_t)nblk, sizeof(cand_t), by_neg_score_then_pos);

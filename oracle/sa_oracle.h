@@ -106,13 +106,17 @@ int orc_masked_mla(const double* q_lat, const double* q_rope,
  *   [0, n_sink), union window [L - n_win, L); one softmax with scale sm_scale
  *   over the union; output o[b, h, :] = sum softmax * v.
  *   blocks_out[B, Hq, nsel] (may be NULL) receives the selected block indices
- *   in ascending order. */
+ *   in ascending order.
+ *   shared != 0: the block choice is shared by the query heads of a KV group,
+ *   by the sum of their block scores, ties to the lower block index
+ *   ["MLA 与稀疏注意力" section on block choice and merging, worked example]. */
 int orc_block_pool(const double* k, int B, int L, int Hkv, int d, int blk,
                    double* krep);
 int orc_block_sparse_decode(const double* q, const double* k, const double* v,
                             const double* krep, int B, int L, int Hq, int Hkv,
                             int d, int blk, int nsel, int n_sink, int n_win,
-                            double sm_scale, double* out, int32_t* blocks_out);
+                            double sm_scale, int shared, double* out,
+                            int32_t* blocks_out);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,8 @@ scores them in double).  Chosen sets must have equal sizes and may differ only
 by blocks whose oracle score is within 1e-3 of the nsel-th score (relative);
 the attention output is compared (max-abs 2e-3, bf16 inputs) for every head
 whose chosen set equals the oracle's, which on continuous random data is every
-head.
+head.  With a shared choice the scores are the KV group's sums, and every head
+of a group must carry the same set.
 """
 import sys
 
@@ -27,14 +28,18 @@ def _announce(msg):
     print(f"\n[block] {msg}", file=sys.stderr, flush=True)
 
 
-def _block_scores(q, krep, Hkv):
-    """Oracle-precision block scores q_h . krep[b, n, g(h)] -> [B, Hq, nblk]."""
+def _block_scores(q, krep, Hkv, shared=False):
+    """Oracle-precision block scores q_h . krep[b, n, g(h)] -> [B, Hq, nblk];
+    with shared=True each head gets its KV group's sum."""
     qd = oracle.decode(q)
     kr = oracle.decode(krep)
     B, Hq, d = qd.shape
     G = Hq // Hkv
     krg = np.repeat(kr, G, axis=2)  # [B, nblk, Hq, d]
-    return np.einsum("bhd,bnhd->bhn", qd, krg)
+    sc = np.einsum("bhd,bnhd->bhn", qd, krg)
+    if shared:
+        sc = np.repeat(sc.reshape(B, Hkv, G, -1).sum(axis=2), G, axis=1)
+    return sc
 
 
 def _check_choice(g_blocks, o_blocks, scores, nsel):
@@ -62,19 +67,28 @@ def _check_choice(g_blocks, o_blocks, scores, nsel):
     return same
 
 
-def _run_case(wl, check_units=None):
+def _same_within_groups(blocks, Hkv):
+    b = blocks.cpu().numpy()
+    B, Hq, nsel = b.shape
+    g = b.reshape(B, Hkv, Hq // Hkv, nsel)
+    assert (g == g[:, :, :1]).all(), "heads of a KV group chose different blocks"
+
+
+def _run_case(wl, shared=False):
     t = wl.to(DEV)
     krep = api.sparse_attn_block_pool(t.k, wl.blk)
     out, blocks = api.sparse_attn_block_decode(t.q, t.k, t.v, krep, wl.blk, wl.nsel, wl.n_sink,
-                                               wl.n_win, wl.sm_scale)
+                                               wl.n_win, wl.sm_scale, shared_choice=shared)
     torch.cuda.synchronize()
+    if shared:
+        _same_within_groups(blocks, wl.Hkv)
     # pooled keys against the oracle's mean in double
     okr = oracle.block_pool(wl.k, wl.blk)
     gkr = krep.cpu().numpy().astype(np.float64)
     assert np.allclose(gkr, okr, rtol=1e-5, atol=1e-6), "pooled keys differ"
     ro, rb = oracle.block_sparse_decode(wl.q, wl.k, wl.v, wl.blk, wl.nsel, wl.n_sink, wl.n_win,
-                                        wl.sm_scale, krep=krep.cpu())
-    sc = _block_scores(wl.q, krep.cpu(), wl.Hkv)
+                                        wl.sm_scale, krep=krep.cpu(), shared=shared)
+    sc = _block_scores(wl.q, krep.cpu(), wl.Hkv, shared)
     same = _check_choice(blocks, rb, sc, wl.nsel)
     assert same.mean() > 0.9, "too many heads with near-tie choices"
     err = np.abs(out.cpu().numpy().astype(np.float64) - ro)
@@ -130,3 +144,35 @@ def test_block_sparse_fullsize_sampled():
         same = _check_choice(blocks[b:b + 1], rb, sc, wl.nsel)
         err = np.abs(out[b:b + 1].cpu().numpy().astype(np.float64) - ro)
         assert err.max(axis=-1)[same].max() <= ATTN_ATOL_BF16
+
+
+@pytest.mark.parametrize("blk,G", [(64, 4), (32, 8), (128, 2)])
+def test_block_sparse_shared_choice(blk, G):
+    _announce(f"block sparse, group-shared choice, blk={blk} G={G}")
+    Hkv = 2
+    wl = workloads.block_sparse_64k(B=2, L=4133, Hq=G * Hkv, Hkv=Hkv, blk=blk, nsel=10,
+                                    n_sink=16, n_win=150)
+    _run_case(wl, shared=True)
+
+
+def test_block_sparse_shared_choice_fullsize_sampled():
+    """The block-sparse workload at full size with the group-shared choice;
+    one sequence goes to the oracle."""
+    _announce("block sparse full size, group-shared choice")
+    wl = workloads.block_sparse_64k()
+    t = wl.to(DEV)
+    krep = api.sparse_attn_block_pool(t.k, wl.blk)
+    out, blocks = api.sparse_attn_block_decode(t.q, t.k, t.v, krep, wl.blk, wl.nsel, wl.n_sink,
+                                               wl.n_win, wl.sm_scale, shared_choice=True)
+    torch.cuda.synchronize()
+    _same_within_groups(blocks, wl.Hkv)
+    b = wl.B // 2
+    _announce(f"oracle on sequence {b}")
+    q, k, v = wl.q[b:b + 1], wl.k[b:b + 1], wl.v[b:b + 1]
+    kr = krep[b:b + 1].cpu()
+    ro, rb = oracle.block_sparse_decode(q, k, v, wl.blk, wl.nsel, wl.n_sink, wl.n_win,
+                                        wl.sm_scale, krep=kr, shared=True)
+    sc = _block_scores(q, kr, wl.Hkv, shared=True)
+    same = _check_choice(blocks[b:b + 1], rb, sc, wl.nsel)
+    err = np.abs(out[b:b + 1].cpu().numpy().astype(np.float64) - ro)
+    assert err.max(axis=-1)[same].max() <= ATTN_ATOL_BF16

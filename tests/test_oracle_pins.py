@@ -533,3 +533,63 @@ def test_block_sparse_all_blocks_is_dense(orc):
     out, _ = orc.block_sparse_decode(q, k, v, blk, L // blk, 0, 0, 0.5)
     ref = _sdpa_masked(q[0], k[0], v[0], torch.ones(Hq, L, dtype=torch.bool), 0.5)
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# GQA-shared block choice (the group's heads share one block set)
+# --------------------------------------------------------------------------
+
+def test_gqa_shared_choice_page_example(orc, ex):
+    # two heads over three blocks; block keys are unit vectors, so each head's
+    # block scores are exactly the page's numbers
+    e = ex["gqa_shared_choice"]
+    sc = torch.tensor(e["head_scores"], dtype=torch.float64)  # [2 heads, 3 blocks]
+    Hq, nblk = sc.shape
+    q = sc[None].clone()                                       # [1, 2, d=3]
+    k = torch.eye(nblk, dtype=torch.float64)[None, :, None, :]  # blk = 1: krep = k
+    g = torch.Generator().manual_seed(15)
+    v = torch.randn(1, nblk, 1, nblk, generator=g, dtype=torch.float64)
+    _, own = orc.block_sparse_decode(q, k, v, 1, 1, 0, 0, 1.0)
+    assert own[0, :, 0].tolist() == e["per_head_top1"]
+    out, shared = orc.block_sparse_decode(q, k, v, 1, 1, 0, 0, 1.0, shared=True)
+    assert shared[0, :, 0].tolist() == e["group_top1"] * Hq
+    # one visible token: the output is its value row
+    for h in range(Hq):
+        np.testing.assert_array_equal(out[0, h], v[0, e["group_top1"][0], 0].numpy())
+
+
+def test_gqa_shared_choice_sums_group_scores(orc):
+    g = torch.Generator().manual_seed(16)
+    B, L, Hq, Hkv, d, blk = 2, 96, 8, 2, 8, 8
+    q = torch.randn(B, Hq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, L, Hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, L, Hkv, d, generator=g, dtype=torch.float64)
+    nsel, n_sink, n_win = 3, 2, 5
+    out, blocks = orc.block_sparse_decode(q, k, v, blk, nsel, n_sink, n_win, 0.4, shared=True)
+    rep = orc.block_pool(k, blk)
+    G = Hq // Hkv
+    for b in range(B):
+        mask = torch.zeros(Hq, L, dtype=torch.bool)
+        for h in range(Hq):
+            gh = h // G
+            tot = sum(rep[b, :, gh] @ q[b, hh].numpy() for hh in range(gh * G, gh * G + G))
+            order = sorted(range(L // blk), key=lambda i: (-tot[i], i))[:nsel]
+            assert blocks[b, h].tolist() == sorted(order)
+            for bi in order:
+                mask[h, bi * blk:(bi + 1) * blk] = True
+            mask[h, :n_sink] = True
+            mask[h, L - n_win:] = True
+        ref = _sdpa_masked(q[b], k[b], v[b], mask, 0.4)
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_shared_choice_group_of_one_is_per_head(orc):
+    g = torch.Generator().manual_seed(17)
+    B, L, H, d, blk = 1, 64, 3, 4, 8
+    q = torch.randn(B, H, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, L, H, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, L, H, d, generator=g, dtype=torch.float64)
+    o1, b1 = orc.block_sparse_decode(q, k, v, blk, 2, 1, 4, 0.5)
+    o2, b2 = orc.block_sparse_decode(q, k, v, blk, 2, 1, 4, 0.5, shared=True)
+    assert np.array_equal(b1, b2)
+    np.testing.assert_array_equal(o1, o2)

@@ -58,8 +58,8 @@ def load():
     L.sparse_attn_decode.argtypes = [P, I, P, P, I, P, P, I, I, I, I, I, P, P, I, P, P, I,
                                      I64, I64, I, I, I, F, P, P, P, P, SZ, P]
     L.sparse_attn_block_pool.argtypes = [P, I, I, I, I, I, P, P]
-    L.sparse_attn_block_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, P,
-                                           P, SZ, P]
+    L.sparse_attn_block_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
+                                           P, P, SZ, P]
     L.sparse_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.sparse_attn_workspace_bytes.restype = SZ
     L.sparse_attn_status_string.argtypes = [I]
@@ -265,8 +265,9 @@ def sparse_attn_block_pool(k, blk, krep=None, stream=None):
 
 
 def sparse_attn_block_decode(q, k, v, krep, blk, nsel, n_sink, n_win, sm_scale, out=None,
-                             blocks_out=None, ws=None, stream=None):
-    """GQA block-sparse decode -> (out [B,Hq,d] fp32, blocks [B,Hq,nsel] int32)."""
+                             blocks_out=None, ws=None, stream=None, shared_choice=False):
+    """GQA block-sparse decode -> (out [B,Hq,d] fp32, blocks [B,Hq,nsel] int32).
+    shared_choice: the heads of a KV group share one block choice."""
     B, Hq, d = q.shape
     L, Hkv = k.shape[1], k.shape[2]
     _need(q, "q", (torch.bfloat16,))
@@ -283,6 +284,6 @@ def sparse_attn_block_decode(q, k, v, krep, blk, nsel, n_sink, n_win, sm_scale, 
     ws, nb = _workspace(ws, sparse_attn_workspace_bytes(SA_OP_BLOCK_DECODE, B, Hq, L, nsel, Hkv,
                                                         d), dev)
     _call("sparse_attn_block_decode", _ptr(q), _ptr(k), _ptr(v), _ptr(krep), B, L, Hq, Hkv, d,
-          blk, nsel, n_sink, n_win, float(sm_scale), _ptr(out), _ptr(blocks_out), _ptr(ws), nb,
-          _stream(stream))
+          blk, nsel, n_sink, n_win, float(sm_scale), int(bool(shared_choice)), _ptr(out),
+          _ptr(blocks_out), _ptr(ws), nb, _stream(stream))
     return out, blocks_out

@@ -203,10 +203,13 @@ int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk,
 
 int sparse_attn_block_decode(const void* q, const void* k, const void* v, const float* krep, int B,
                              int L, int Hq, int Hkv, int d, int blk, int nsel, int n_sink,
-                             int n_win, float sm_scale, float* out, int32_t* blocks_out, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             int n_win, float sm_scale, int shared_choice, float* out,
+                             int32_t* blocks_out, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  sa::BlockArgs a{q, k, v, krep, B, L, Hq, Hkv, d, blk, nsel, n_sink, n_win, sm_scale, out, blocks_out, ws};
+  sa::BlockArgs a{q, k, v, krep, B, L, Hq, Hkv, d, blk, nsel, n_sink, n_win, sm_scale,
+                  shared_choice, out, blocks_out, ws};
+  REQUIRE(shared_choice == 0 || shared_choice == 1, SA_ERR_SHAPE,
+          "block_decode: shared_choice must be 0 or 1");
   REQUIRE(q && k && v && krep && out, SA_ERR_NULL, "block_decode: q, k, v, krep and out are required");
   REQUIRE(B >= 0 && L >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && n_sink >= 0 && n_win >= 0 && nsel >= 1,
           SA_ERR_SHAPE, "block_decode: bad size");

@@ -92,6 +92,7 @@ struct BlockSelArgs {
   const uint16_t* q;    // [B, Hq, d]
   const float* krep;    // [B, nblk, Hkv, d]
   int Hq, Hkv, nblk, nsel;
+  int shared;           // score with the sum of the KV group's queries
   int32_t* chosen;      // [B, Hq, nsel] (workspace)
   int32_t* blocks_out;  // [B, Hq, nsel] or null
 };
@@ -118,21 +119,27 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
   __shared__ int pick[kBlkMaxSel];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
-  const int g = h / (a.Hq / a.Hkv), nblk = a.nblk;
+  const int G = a.Hq / a.Hkv, g = h / G, nblk = a.nblk;
+  // the head's query, or with a shared choice the sum of the group's queries:
+  // the sum of the heads' block scores is the group-sum query's score, so the
+  // group's work-groups all reach the same choice
   float qf[kBlkD];
-  {
-    const uint4* qp = (const uint4*)(a.q + ((int64_t)b * a.Hq + h) * kBlkD);
+#pragma unroll
+  for (int i = 0; i < kBlkD; ++i) qf[i] = 0.f;
+  const int h0 = a.shared ? g * G : h, h1 = a.shared ? h0 + G : h + 1;
+  for (int hh = h0; hh < h1; ++hh) {
+    const uint4* qp = (const uint4*)(a.q + ((int64_t)b * a.Hq + hh) * kBlkD);
 #pragma unroll
     for (int i = 0; i < kBlkD / 8; ++i) {
       const uint4 u = qp[i];
-      qf[8 * i + 0] = bf16_lo(u.x);
-      qf[8 * i + 1] = bf16_hi(u.x);
-      qf[8 * i + 2] = bf16_lo(u.y);
-      qf[8 * i + 3] = bf16_hi(u.y);
-      qf[8 * i + 4] = bf16_lo(u.z);
-      qf[8 * i + 5] = bf16_hi(u.z);
-      qf[8 * i + 6] = bf16_lo(u.w);
-      qf[8 * i + 7] = bf16_hi(u.w);
+      qf[8 * i + 0] += bf16_lo(u.x);
+      qf[8 * i + 1] += bf16_hi(u.x);
+      qf[8 * i + 2] += bf16_lo(u.y);
+      qf[8 * i + 3] += bf16_hi(u.y);
+      qf[8 * i + 4] += bf16_lo(u.z);
+      qf[8 * i + 5] += bf16_hi(u.z);
+      qf[8 * i + 6] += bf16_lo(u.w);
+      qf[8 * i + 7] += bf16_hi(u.w);
     }
   }
   // block n = tid + 256 r: one pooled-key row (512 bytes) per lane
@@ -424,6 +431,7 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   s.Hkv = a.Hkv;
   s.nblk = nblk;
   s.nsel = a.nsel;
+  s.shared = a.shared_choice;
   s.chosen = (int32_t*)a.ws;
   s.blocks_out = a.blocks_out;
   block_select_kernel<<<dim3(a.Hq, a.B), 256, 0, st>>>(s);

@@ -64,6 +64,7 @@ struct BlockArgs {
   const float* krep;
   int B, L, Hq, Hkv, d, blk, nsel, n_sink, n_win;
   float sm_scale;
+  int shared_choice;  // 1: one block choice per KV group (sum of its heads' scores)
   float* out;
   int32_t* blocks_out;
   void* ws;
