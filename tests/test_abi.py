@@ -89,7 +89,13 @@ def test_topk_validation(lib):
     # a long row needs a workspace
     assert f(A, None, None, 1, 1, 100000, 2048, A, None, None, 0, None) == 6
     assert lib.sparse_attn_workspace_bytes(0, 1, 1, 100000, 2048, 0, 0) > 0
-    assert lib.sparse_attn_workspace_bytes(0, 1, 1, 32768, 2048, 0, 0) == 0
+    # few rows of >= 8192 positions are split over work-groups: per row and
+    # 4096-position chunk, four counts, the bracket and 4096 (key, position)
+    assert lib.sparse_attn_workspace_bytes(0, 1, 1, 32768, 2048, 0, 0) == 8 * (24 + 8 * 4096)
+    assert f(A, None, None, 1, 1, 32768, 2048, A, None, None, 0, None) == 6
+    # rows that fill the GPU, and short rows, need none
+    assert lib.sparse_attn_workspace_bytes(0, 1, 200, 32768, 2048, 0, 0) == 0
+    assert lib.sparse_attn_workspace_bytes(0, 1, 1, 4096, 2048, 0, 0) == 0
 
 
 def test_mla_validation(lib):

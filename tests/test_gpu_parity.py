@@ -119,16 +119,24 @@ def test_topk_exact_small_integer_workload():
     assert np.array_equal(gc, oc) and np.array_equal(gi, oi)
 
 
-@pytest.mark.parametrize("L,k,kind", [(5000, 2048, "normal"), (32768, 2048, "ties"),
-                                      (32768, 4096, "signed"), (1000, 1, "ties"),
-                                      (70000, 2048, "ties"), (131072, 2048, "normal"),
-                                      (40000, 64, "zeros"), (70000, 2048, "narrow"),
-                                      (70000, 2048, "allequal")])
-def test_topk_matches_oracle_bitexact(L, k, kind):
-    _announce(f"topk L={L} k={k} {kind}")
+# Few rows of length >= 8192 take the split path (chunk work-groups + one
+# select work-group per row, with a fallback from the row itself); the other
+# shapes and the many-row cases take one work-group per row (chunks and a merge
+# beyond 32768 positions).
+@pytest.mark.parametrize("L,k,kind,B", [(5000, 2048, "normal", 3), (32768, 2048, "ties", 3),
+                                        (32768, 4096, "signed", 3), (1000, 1, "ties", 3),
+                                        (70000, 2048, "ties", 3), (131072, 2048, "normal", 3),
+                                        (40000, 64, "zeros", 3), (70000, 2048, "narrow", 3),
+                                        (70000, 2048, "allequal", 3), (32768, 2048, "hidden", 3),
+                                        (12345, 300, "normal", 3), (40000, 512, "ties", 130)])
+def test_topk_matches_oracle_bitexact(L, k, kind, B):
+    _announce(f"topk L={L} k={k} {kind} rows={B}")
     g0 = torch.Generator().manual_seed(L + k)
-    B = 3
-    if kind == "normal":
+    if kind == "hidden":
+        # the largest scores sit on positions the row sample never visits
+        s = torch.rand(B, 1, L, generator=g0)
+        s[:, :, 1::16] += 10.0
+    elif kind == "normal":
         s = torch.randn(B, 1, L, generator=g0).abs()
     elif kind == "ties":
         s = torch.randint(0, 40, (B, 1, L), generator=g0).float() * 0.25
@@ -144,8 +152,8 @@ def test_topk_matches_oracle_bitexact(L, k, kind):
     else:
         s = torch.randn(B, 1, L, generator=g0) * 1e3
         s[:, :, ::7] = -s[:, :, ::7].abs()
-    kv_len = torch.tensor([L, L // 2 + 3, min(k, L) - 1 if min(k, L) > 1 else 1],
-                          dtype=torch.int32)
+    kv_len = torch.tensor([L, L // 2 + 3, min(k, L) - 1 if min(k, L) > 1 else 1] * (B // 3) +
+                          [L] * (B % 3), dtype=torch.int32)
     gi, gc, oi, oc = _topk_both(s, k, kv_len=kv_len)
     assert np.array_equal(gc, oc)
     assert np.array_equal(gi, oi)

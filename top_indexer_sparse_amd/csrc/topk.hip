@@ -32,6 +32,9 @@
 // chunk keeps its own top-k (a superset of its share of the row's top-k under
 // the same rule), and a second launch selects from the chunks' candidates,
 // which are laid out in ascending position order, so the tie rule carries over.
+// Launches with few rows of 8192 or more positions (decode) take the split
+// path further down instead: 4096-position chunk work-groups around a
+// sampled key bracket, then one select work-group per row.
 #include <math.h>
 
 #include "common.hpp"
@@ -516,6 +519,409 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
   if (out_count && tid == 0) *out_count = n_sel;
 }
 
+// ---------------------------------------------------------------------------
+// Split path: few long rows (decode).  One work-group per row leaves most of
+// the GPU idle and runs every pass over the row on one CU, so a row is cut
+// into 4096-position chunks, one work-group each, in two launches:
+//  A. Every chunk's work-group draws the same deterministic sample of its row
+//     (128 evenly spaced runs of 16 positions) and from it the same key
+//     bracket [lo, hi] around the expected rank of the k-th key (four
+//     standard deviations of the sample rank).  It keeps the keys >= lo of
+//     its chunk, with their positions, compacted in position order, and
+//     counts those above hi, those inside, and the candidates at all.
+//  B. One work-group per row checks the bracket against the chunks' counts
+//     (above < k <= above + inside).  Radix passes over the inside keys give
+//     tau, the k-th largest key; one block scan over the kept keys in
+//     position order then places every selected position (keys > tau, and
+//     keys == tau up to k, lowest positions first) at its ascending slot.
+//     When the bracket misses, the kept keys overflow, or the row has at most
+//     k candidates, the same work-group selects straight from the row's
+//     scores instead (radix passes over the whole row), so correctness never
+//     rests on the sample.
+// ---------------------------------------------------------------------------
+constexpr int kSpChunk = 4096;
+constexpr int kSpThreads = 256;
+constexpr int kSpWaves = kSpThreads / 64;
+constexpr int kSpPer = kSpChunk / kSpThreads;  // consecutive positions per thread
+constexpr int kSpRuns = 128, kSpRun = 16;      // the row sample: 2048 keys
+constexpr int kSpSamplePer = kSpRuns * kSpRun / kSpThreads;
+constexpr int kSpBins = 2048;
+constexpr int kSpMaxRows = 128;    // rows of a launch taking the split path
+constexpr int kSpMinL = 8192;      // shortest row length taking it
+constexpr int kSpMaxChunks = 256;  // rows up to 1M positions
+constexpr int kSpKeep = 16384;     // kept keys the second launch holds in LDS
+
+struct TopkSplitArgs {
+  const float* scores;
+  const int32_t* q_pos;
+  const int32_t* kv_len;
+  int T, L, k, nchunk;
+  int vec4;            // scores rows are 16-byte aligned (float4 loads)
+  int32_t* cnt;        // [rows][nchunk][4]: above, inside, candidates, -
+  uint32_t* bracket;   // [rows][nchunk][2]: lo, hi (equal in every chunk)
+  uint32_t* keepk;     // [rows][nchunk][kSpChunk]: kept keys (>= lo), position order
+  int32_t* keepp;      // [rows][nchunk][kSpChunk]: their positions
+  int32_t* idx;        // [rows][k]
+  int32_t* count;      // [rows] or null
+};
+
+// Exclusive block scan over the 256 threads of a split work-group.
+__device__ __forceinline__ int sp_scan_excl(int x, int* red, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int incl = wave_scan_incl(x);
+  __syncthreads();
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kSpWaves; ++w) {
+    const int v = red[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  return incl - x + before;
+}
+
+// Bin of `hist` (2048 bins) holding rank r counted from the top, and the
+// number of entries in higher bins; r outside [1, total] gives bin -1.
+// Thread t owns bins 2047 - 8t .. 2040 - 8t.  Starts with a barrier (the
+// histogram is complete); `found` is visible when it returns.
+__device__ __forceinline__ void sp_rank_bin(const int* hist, int r, int* red, int* found) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    found[0] = -1;
+    found[1] = 0;
+  }
+  int h[8], own = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = hist[kSpBins - 1 - 8 * tid - e];
+    own += h[e];
+  }
+  int total;
+  int above = sp_scan_excl(own, red, total);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (above < r && r <= above + h[e]) {
+      found[0] = kSpBins - 1 - 8 * tid - e;
+      found[1] = above;
+    }
+    above += h[e];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int sp_block_sum(int x, int* red) {
+  const int t = wave_total(x);
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kSpWaves; ++w) total += red[w];
+  return total;
+}
+
+// Launch A: one work-group per (chunk, row).
+__global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitArgs a) {
+  __shared__ int hist[kSpBins];
+  __shared__ int red[kSpWaves];
+  __shared__ uint32_t rmin[kSpWaves], rmax[kSpWaves];
+  __shared__ int found[2];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int chunk = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / a.T);
+  const int lim = candidate_limit(a.q_pos, a.kv_len, b, row, a.L);
+  const float* srow = a.scores + row * a.L;
+  const int c0 = chunk * kSpChunk;
+  const int64_t unit = row * a.nchunk + chunk;
+  int32_t* cnt = a.cnt + unit * 4;
+  if (c0 >= lim) {  // nothing of the row here
+    if (tid == 0) cnt[0] = cnt[1] = cnt[2] = cnt[3] = 0;
+    return;
+  }
+  // this thread's 16 consecutive positions and its 8 sample positions, all
+  // loads issued before any is used
+  const int p0 = c0 + kSpPer * tid;
+  float cs[kSpPer];
+  if (a.vec4 && p0 + kSpPer <= lim) {
+#pragma unroll
+    for (int i = 0; i < kSpPer / 4; ++i) {
+      const float4 v = *(const float4*)(srow + p0 + 4 * i);
+      cs[4 * i] = v.x;
+      cs[4 * i + 1] = v.y;
+      cs[4 * i + 2] = v.z;
+      cs[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSpPer; ++i) cs[i] = p0 + i < lim ? srow[p0 + i] : -INFINITY;
+  }
+  // sample: run r = tid / 2 starts at r * lim / 128 (every position when the
+  // row is shorter than the sample)
+  const int sbase = lim >= kSpRuns * kSpRun
+                        ? (int)((int64_t)(tid >> 1) * lim / kSpRuns) + kSpSamplePer * (tid & 1)
+                        : kSpSamplePer * tid;
+  float ss[kSpSamplePer];
+#pragma unroll
+  for (int m = 0; m < kSpSamplePer; ++m) ss[m] = sbase + m < lim ? srow[sbase + m] : -INFINITY;
+  const int S = min(lim, kSpRuns * kSpRun);
+
+  // ---- the row's bracket from the sample (identical in every chunk) ----
+  uint32_t sk[kSpSamplePer];
+  int nv = 0;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int m = 0; m < kSpSamplePer; ++m) {
+    sk[m] = score_key(ss[m]);
+    nv += sk[m] != 0u;
+    mn = sk[m] ? min(mn, sk[m]) : mn;
+    mx = max(mx, sk[m]);
+  }
+  nv = wave_total(nv);
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  for (int i = tid; i < kSpBins; i += kSpThreads) hist[i] = 0;
+  if (lane == 0) {
+    red[wave] = nv;
+    rmin[wave] = mn;
+    rmax[wave] = mx;
+  }
+  __syncthreads();
+  int ns = 0;
+  uint32_t smin = 0xffffffffu, smax = 0u;
+#pragma unroll
+  for (int w = 0; w < kSpWaves; ++w) {
+    ns += red[w];
+    smin = min(smin, rmin[w]);
+    smax = max(smax, rmax[w]);
+  }
+  uint32_t lo = 1u, hi = 0xffffffffu;  // no usable sample: every candidate is inside
+  if (ns > 0) {
+    const int sh = max(0, 32 - __clz(smax - smin) - 11);  // (range >> sh) < 2048
+#pragma unroll
+    for (int m = 0; m < kSpSamplePer; ++m) hist_add(hist, (sk[m] - smin) >> sh, sk[m] != 0u);
+    // sample ranks, counted from the top, that bracket the row's k-th key
+    const float p = fminf(1.f, (float)a.k / (float)lim);
+    const float mean = p * (float)S;
+    const float margin = 4.f * sqrtf(mean * (1.f - p)) + 2.f;
+    const int r0 = min(max(1, (int)floorf(mean - margin)), ns);
+    const int r1u = (int)ceilf(mean + margin);
+    const int r1 = min(max(r1u, r0), ns);
+    sp_rank_bin(hist, r0, red, found);
+    const int bhi = found[0];
+    sp_rank_bin(hist, r1, red, found);
+    const int blo = found[0];
+    hi = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)smin + ((uint64_t)(bhi + 1) << sh) - 1u);
+    lo = r1u > ns ? 1u : smin + ((uint32_t)blo << sh);
+  }
+
+  // ---- this chunk: the keys >= lo, compacted in position order ----
+  uint32_t ck[kSpPer];
+  int na = 0, nk = 0, nc = 0;
+#pragma unroll
+  for (int i = 0; i < kSpPer; ++i) {
+    ck[i] = score_key(cs[i]);
+    nc += ck[i] != 0u;
+    na += ck[i] > hi;
+    nk += ck[i] != 0u && ck[i] >= lo;
+  }
+  int tot_packed;
+  int o = sp_scan_excl((na << 16) | nk, red, tot_packed) & 0xffff;
+  const int64_t base = unit * (int64_t)kSpChunk;
+#pragma unroll
+  for (int i = 0; i < kSpPer; ++i) {
+    if (ck[i] != 0u && ck[i] >= lo) {
+      a.keepk[base + o] = ck[i];
+      a.keepp[base + o] = p0 + i;
+      ++o;
+    }
+  }
+  const int nct = sp_block_sum(nc, red);
+  if (tid == 0) {
+    cnt[0] = tot_packed >> 16;                            // above hi
+    cnt[1] = (tot_packed & 0xffff) - (tot_packed >> 16);  // inside [lo, hi]
+    cnt[2] = nct;                                         // candidates
+    cnt[3] = 0;
+    a.bracket[2 * unit] = lo;
+    a.bracket[2 * unit + 1] = hi;
+  }
+}
+
+// Launch B: one 256-thread work-group per row.
+__global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplitArgs a) {
+  __shared__ uint32_t kk[kSpKeep];
+  __shared__ int32_t kp[kSpKeep];
+  __shared__ int hist[kSpBins];
+  __shared__ int red[kSpWaves];
+  __shared__ int found[2];
+  __shared__ int preK[kSpMaxChunks + 1];
+  __shared__ int tot[4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int k = a.k;
+  const int b = (int)(row / a.T);
+  const int lim = candidate_limit(a.q_pos, a.kv_len, b, row, a.L);
+  const int nch = min(a.nchunk, (lim + kSpChunk - 1) / kSpChunk);
+  int32_t* out = a.idx + row * k;
+
+  // ---- the chunks' counts -> offsets of their kept keys ----
+  {
+    const int32_t* cnt = a.cnt + row * a.nchunk * 4;
+    int ca = 0, ci = 0, cc = 0;
+    if (tid < nch) {
+      const int4 c4 = *(const int4*)(cnt + 4 * tid);
+      ca = c4.x;
+      ci = c4.y;
+      cc = c4.z;
+    }
+    int tK;
+    const int ek = sp_scan_excl(ca + ci, red, tK);
+    const int tA = sp_block_sum(ca, red);
+    const int tC = sp_block_sum(cc, red);
+    if (tid < nch) preK[tid] = ek;
+    if (tid == 0) {
+      preK[nch] = tK;
+      tot[0] = tA;
+      tot[1] = tK - tA;
+      tot[2] = tC;
+    }
+    __syncthreads();
+  }
+  const int A = tot[0], I = tot[1], V = tot[2], K = A + I;
+  const int n_sel = min(k, V);
+  const bool fast = V > k && A < k && K >= k && K <= kSpKeep;
+
+  if (fast) {
+    const uint32_t lo = a.bracket[2 * row * a.nchunk], hi = a.bracket[2 * row * a.nchunk + 1];
+    // ---- kept keys into LDS (chunk order = position order): 256 / nch
+    //      threads per chunk, 16 loads in flight per thread and batch ----
+    {
+      const int tpc = kSpThreads / nch;  // >= 1
+      const int c = tid / tpc, r = tid % tpc;
+      if (c < nch) {
+        const int n_c = preK[c + 1] - preK[c];
+        const int d0 = preK[c];
+        const int64_t src0 = (row * a.nchunk + c) * (int64_t)kSpChunk;
+        for (int i0 = r; i0 < n_c; i0 += 16 * tpc) {
+          uint32_t vk[16];
+          int32_t vp[16];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int i = min(i0 + tpc * m, n_c - 1);
+            vk[m] = a.keepk[src0 + i];
+            vp[m] = a.keepp[src0 + i];
+          }
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int i = i0 + tpc * m;
+            if (i < n_c) {
+              kk[d0 + i] = vk[m];
+              kp[d0 + i] = vp[m];
+            }
+          }
+        }
+      }
+    }
+    // ---- tau: the (k - A)-th largest inside key, by radix passes over the
+    //      offsets key - lo (11 bits at a time, from the top) ----
+    int krem = k - A;
+    uint32_t prefix = 0u, pmask = 0u;
+    const uint32_t span = hi - lo;
+    int top = span ? 31 - __clz(span) : -1;
+#pragma unroll 1
+    while (top >= 0) {
+      const int width = min(11, top + 1);
+      const int s2 = top + 1 - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      __syncthreads();  // kept keys stored / previous bins read
+      for (int i = tid; i < kSpBins; i += kSpThreads) hist[i] = 0;
+      __syncthreads();
+#pragma unroll 1
+      for (int j0 = 0; j0 < K; j0 += kSpThreads) {
+        const int j = j0 + tid;
+        const uint32_t key = j < K ? kk[j] : 0u;
+        const uint32_t c = key - lo;
+        hist_add(hist, (c >> s2) & dmask, j < K && key <= hi && (c & pmask) == prefix);
+      }
+      sp_rank_bin(hist, krem, red, found);
+      prefix |= (uint32_t)found[0] << s2;
+      pmask |= dmask << s2;
+      krem -= found[1];
+      top = s2 - 1;
+    }
+    const uint32_t tau = lo + prefix;
+    const int need_eq = krem;
+    // ---- ascending output: thread t scans its run of the kept keys ----
+    __syncthreads();
+    const int s = (K + kSpThreads - 1) / kSpThreads;  // <= 64
+    const int j0 = tid * s, j1 = min(K, j0 + s);
+    int c = 0;
+    for (int j = j0; j < j1; ++j) c += ((kk[j] > tau) << 16) | (kk[j] == tau);
+    int total;
+    const int before = sp_scan_excl(c, red, total);  // gt, eq <= 16384 each
+    int gtb = before >> 16, eqb = before & 0xffff;
+    for (int j = j0; j < j1; ++j) {
+      const bool g = kk[j] > tau, eq = kk[j] == tau;
+      if (g || (eq && eqb < need_eq)) out[gtb + min(eqb, need_eq)] = kp[j];
+      gtb += g;
+      eqb += eq;
+    }
+  } else {
+    // ---- straight from the row: radix passes over all its keys ----
+    const float* srow = a.scores + row * a.L;
+    uint32_t tau = 0u;  // V <= k: every candidate (key > 0) is taken
+    int need_eq = 0;
+    if (V > k) {
+      int krem = k;
+      uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll 1
+      for (int pass = 0; pass < 3; ++pass) {
+        const int s2 = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+        const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
+        __syncthreads();
+        for (int i = tid; i < kSpBins; i += kSpThreads) hist[i] = 0;
+        __syncthreads();
+#pragma unroll 1
+        for (int q0 = 0; q0 < lim; q0 += kSpThreads) {
+          const int q = q0 + tid;
+          const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
+          hist_add(hist, (c >> s2) & dmask, c != 0u && (c & pmask) == prefix);
+        }
+        sp_rank_bin(hist, krem, red, found);
+        prefix |= (uint32_t)found[0] << s2;
+        pmask |= dmask << s2;
+        krem -= found[1];
+      }
+      tau = prefix;
+      need_eq = krem;
+    }
+    // emission in position order, 256 positions per round
+    int run_gt = 0, run_eq = 0;
+#pragma unroll 1
+    for (int q0 = 0; q0 < lim; q0 += kSpThreads) {
+      const int q = q0 + tid;
+      const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
+      const int g = c != 0u && c > tau, eq = c != 0u && c == tau;
+      int total;
+      const int before = sp_scan_excl((g << 16) | eq, red, total);
+      const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
+      if (g || (eq && eqb < need_eq)) out[gtb + min(eqb, need_eq)] = q;
+      run_gt += total >> 16;
+      run_eq += total & 0xffff;
+    }
+  }
+  __syncthreads();
+  for (int i = n_sel + tid; i < k; i += kSpThreads) out[i] = -1;
+  if (a.count && tid == 0) a.count[row] = n_sel;
+}
+
+static bool topk_split(int64_t rows, int L) { return rows <= kSpMaxRows && L >= kSpMinL &&
+                                                     (L + kSpChunk - 1) / kSpChunk <= kSpMaxChunks; }
+
 static int topk_chunks(int L) { return (L + kTkRow - 1) / kTkRow; }
 
 bool topk_supported(int L, int k) {
@@ -525,8 +931,15 @@ bool topk_supported(int L, int k) {
   return nch == 1 || (int64_t)nch * k <= kTkRow;
 }
 
+static size_t split_bytes(int64_t rows, int L) {
+  const int64_t units = rows * ((L + kSpChunk - 1) / kSpChunk);
+  return (size_t)units * (4 * sizeof(int32_t) + 2 * sizeof(uint32_t) +
+                          (size_t)kSpChunk * 2 * sizeof(int32_t));
+}
+
 size_t topk_workspace_bytes(int B, int T, int L, int k) {
   const int64_t rows = (int64_t)B * T;
+  if (topk_split(rows, L)) return split_bytes(rows, L);
   const int nch = topk_chunks(L);
   if (nch <= 1) return 0;
   return (size_t)rows * nch * k * (sizeof(float) + sizeof(int32_t));
@@ -535,6 +948,29 @@ size_t topk_workspace_bytes(int B, int T, int L, int k) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.T;
   if (rows == 0) return hipSuccess;
+  if (topk_split(rows, a.L)) {
+    TopkSplitArgs sp{};
+    sp.scores = a.scores;
+    sp.q_pos = a.q_pos;
+    sp.kv_len = a.kv_len;
+    sp.T = a.T;
+    sp.L = a.L;
+    sp.k = a.k;
+    sp.nchunk = (a.L + kSpChunk - 1) / kSpChunk;
+    sp.vec4 = (a.L % 4 == 0) && ((uintptr_t)a.scores % 16 == 0);
+    const int64_t units = rows * sp.nchunk;
+    sp.cnt = (int32_t*)a.ws;
+    sp.bracket = (uint32_t*)(sp.cnt + units * 4);
+    sp.keepk = sp.bracket + units * 2;
+    sp.keepp = (int32_t*)(sp.keepk + units * kSpChunk);
+    sp.idx = a.idx;
+    sp.count = a.count;
+    topk_split_scan_kernel<<<dim3(sp.nchunk, (unsigned)rows), kSpThreads, 0, st>>>(sp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    topk_split_select_kernel<<<(unsigned)rows, kSpThreads, 0, st>>>(sp);
+    return hipGetLastError();
+  }
   TopkRowArgs r{};
   r.scores = a.scores;
   r.q_pos = a.q_pos;
