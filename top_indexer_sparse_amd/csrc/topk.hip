@@ -583,15 +583,17 @@ __device__ __forceinline__ int sp_scan_excl(int x, int* red, int& total) {
   return incl - x + before;
 }
 
-// Bin of `hist` (2048 bins) holding rank r counted from the top, and the
-// number of entries in higher bins; r outside [1, total] gives bin -1.
-// Thread t owns bins 2047 - 8t .. 2040 - 8t.  Starts with a barrier (the
-// histogram is complete); `found` is visible when it returns.
-__device__ __forceinline__ void sp_rank_bin(const int* hist, int r, int* red, int* found) {
+// Bins of `hist` (2048 bins) holding ranks r0 <= r1 counted from the top:
+// found[0] = bin of r0, found[1] = entries in higher bins, found[2] = bin of
+// r1; a rank outside [1, total] gives bin -1.  Thread t owns bins
+// 2047 - 8t .. 2040 - 8t.  Starts with a barrier (the histogram is
+// complete); `found` is visible when it returns.
+__device__ __forceinline__ void sp_rank_bins(const int* hist, int r0, int r1, int* red,
+                                             int* found) {
   __syncthreads();
   const int tid = threadIdx.x;
   if (tid == 0) {
-    found[0] = -1;
+    found[0] = found[2] = -1;
     found[1] = 0;
   }
   int h[8], own = 0;
@@ -604,13 +606,17 @@ __device__ __forceinline__ void sp_rank_bin(const int* hist, int r, int* red, in
   int above = sp_scan_excl(own, red, total);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    if (above < r && r <= above + h[e]) {
+    if (above < r0 && r0 <= above + h[e]) {
       found[0] = kSpBins - 1 - 8 * tid - e;
       found[1] = above;
     }
+    if (above < r1 && r1 <= above + h[e]) found[2] = kSpBins - 1 - 8 * tid - e;
     above += h[e];
   }
   __syncthreads();
+}
+__device__ __forceinline__ void sp_rank_bin(const int* hist, int r, int* red, int* found) {
+  sp_rank_bins(hist, r, r, red, found);
 }
 
 __device__ __forceinline__ int sp_block_sum(int x, int* red) {
@@ -629,7 +635,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
   __shared__ int hist[kSpBins];
   __shared__ int red[kSpWaves];
   __shared__ uint32_t rmin[kSpWaves], rmax[kSpWaves];
-  __shared__ int found[2];
+  __shared__ int found[3];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int chunk = blockIdx.x;
   const int64_t row = blockIdx.y;
@@ -711,10 +717,8 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
     const int r0 = min(max(1, (int)floorf(mean - margin)), ns);
     const int r1u = (int)ceilf(mean + margin);
     const int r1 = min(max(r1u, r0), ns);
-    sp_rank_bin(hist, r0, red, found);
-    const int bhi = found[0];
-    sp_rank_bin(hist, r1, red, found);
-    const int blo = found[0];
+    sp_rank_bins(hist, r0, r1, red, found);
+    const int bhi = found[0], blo = found[2];
     hi = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)smin + ((uint64_t)(bhi + 1) << sh) - 1u);
     lo = r1u > ns ? 1u : smin + ((uint32_t)blo << sh);
   }
@@ -757,9 +761,11 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
   __shared__ int32_t kp[kSpKeep];
   __shared__ int hist[kSpBins];
   __shared__ int red[kSpWaves];
-  __shared__ int found[2];
+  __shared__ int found[3];
   __shared__ int preK[kSpMaxChunks + 1];
   __shared__ int tot[4];
+  __shared__ uint32_t small[66];
+  __shared__ int nsmall;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int k = a.k;
@@ -832,6 +838,9 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
     uint32_t prefix = 0u, pmask = 0u;
     const uint32_t span = hi - lo;
     int top = span ? 31 - __clz(span) : -1;
+    uint32_t tau = 0u;
+    int need_eq = 0;
+    bool done = false;
 #pragma unroll 1
     while (top >= 0) {
       const int width = min(11, top + 1);
@@ -839,6 +848,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
       const uint32_t dmask = (1u << width) - 1u;
       __syncthreads();  // kept keys stored / previous bins read
       for (int i = tid; i < kSpBins; i += kSpThreads) hist[i] = 0;
+      if (tid == 0) nsmall = 0;
       __syncthreads();
 #pragma unroll 1
       for (int j0 = 0; j0 < K; j0 += kSpThreads) {
@@ -852,9 +862,42 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
       pmask |= dmask << s2;
       krem -= found[1];
       top = s2 - 1;
+      if (top >= 0 && hist[found[0]] <= 64) {
+        // few keys left in the bin: one wave ranks them directly
+#pragma unroll 1
+        for (int j0 = 0; j0 < K; j0 += kSpThreads) {
+          const int j = j0 + tid;
+          const uint32_t key = j < K ? kk[j] : 0u;
+          if (j < K && key <= hi && ((key - lo) & pmask) == prefix) small[atomicAdd(&nsmall, 1)] = key;
+        }
+        __syncthreads();
+        if (tid < 64) {
+          const int n = nsmall;
+          const uint32_t x = tid < n ? small[tid] : 0u;  // kept keys are >= lo >= 1
+          int gt = 0, eq = 0;
+          for (int i = 0; i < n; ++i) {
+            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
+            gt += y > x;
+            eq += y == x;
+          }
+          const uint64_t hit = __ballot(tid < n && gt < krem && krem <= gt + eq);
+          const int lead = __ffsll((unsigned long long)hit) - 1;
+          if (tid == lead) {
+            small[64] = x;
+            small[65] = (uint32_t)(krem - gt);
+          }
+        }
+        __syncthreads();
+        tau = small[64];
+        need_eq = (int)small[65];
+        done = true;
+        break;
+      }
     }
-    const uint32_t tau = lo + prefix;
-    const int need_eq = krem;
+    if (!done) {
+      tau = lo + prefix;
+      need_eq = krem;
+    }
     // ---- ascending output: thread t scans its run of the kept keys ----
     __syncthreads();
     const int s = (K + kSpThreads - 1) / kSpThreads;  // <= 64
