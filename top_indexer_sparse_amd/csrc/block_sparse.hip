@@ -120,27 +120,26 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
   const int G = a.Hq / a.Hkv, g = h / G, nblk = a.nblk;
-  // the head's query, or with a shared choice the sum of the group's queries:
-  // the sum of the heads' block scores is the group-sum query's score, so the
-  // group's work-groups all reach the same choice
+  // the head's query, or with a shared choice the sum of the group's queries
+  // (the sum of the heads' block scores is the group-sum query's score, so
+  // the group's work-groups all reach the same choice), staged in LDS
+  __shared__ float qs[kBlkD];
+  if (tid < kBlkD) {
+    const int h0 = a.shared ? g * G : h, h1 = a.shared ? h0 + G : h + 1;
+    float acc = 0.f;
+    for (int hh = h0; hh < h1; ++hh)
+      acc += bf16_bits_to_float(a.q[((int64_t)b * a.Hq + hh) * kBlkD + tid]);
+    qs[tid] = acc;
+  }
+  __syncthreads();
   float qf[kBlkD];
 #pragma unroll
-  for (int i = 0; i < kBlkD; ++i) qf[i] = 0.f;
-  const int h0 = a.shared ? g * G : h, h1 = a.shared ? h0 + G : h + 1;
-  for (int hh = h0; hh < h1; ++hh) {
-    const uint4* qp = (const uint4*)(a.q + ((int64_t)b * a.Hq + hh) * kBlkD);
-#pragma unroll
-    for (int i = 0; i < kBlkD / 8; ++i) {
-      const uint4 u = qp[i];
-      qf[8 * i + 0] += bf16_lo(u.x);
-      qf[8 * i + 1] += bf16_hi(u.x);
-      qf[8 * i + 2] += bf16_lo(u.y);
-      qf[8 * i + 3] += bf16_hi(u.y);
-      qf[8 * i + 4] += bf16_lo(u.z);
-      qf[8 * i + 5] += bf16_hi(u.z);
-      qf[8 * i + 6] += bf16_lo(u.w);
-      qf[8 * i + 7] += bf16_hi(u.w);
-    }
+  for (int i = 0; i < kBlkD / 4; ++i) {
+    const float4 v = *(const float4*)&qs[4 * i];
+    qf[4 * i] = v.x;
+    qf[4 * i + 1] = v.y;
+    qf[4 * i + 2] = v.z;
+    qf[4 * i + 3] = v.w;
   }
   // block n = tid + 256 r: one pooled-key row (512 bytes) per lane
   uint64_t key[kSelPerLane];
@@ -153,13 +152,13 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
       const float4* kr = (const float4*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD);
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {  // 16 x 16 bytes in flight
-        float4 v[16];
+      for (int c = 0; c < 4; ++c) {  // 8 x 16 bytes in flight
+        float4 v[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = kr[16 * c + i];
+        for (int i = 0; i < 8; ++i) v[i] = kr[8 * c + i];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int d0 = 64 * c + 4 * i;
+        for (int i = 0; i < 8; ++i) {
+          const int d0 = 32 * c + 4 * i;
           acc = fmaf(v[i].x, qf[d0], acc);
           acc = fmaf(v[i].y, qf[d0 + 1], acc);
           acc = fmaf(v[i].z, qf[d0 + 2], acc);
