@@ -467,6 +467,91 @@ def run_block(args, api, dev):
     return result
 
 
+def run_csa(args, api, dev):
+    """Selection over compressed entries: B=32 queries over Lc=32768 entries
+    (a 131072-token context at m = 4), k=2048, 128 window entries, H=128,
+    c=512: indexer + top-k over the entries, then MQA core attention with
+    keys = values = entries over the selection and the window."""
+    import torch
+    from top_indexer_sparse_amd import workloads
+    log("generating csa_decode")
+    wl = workloads.csa_decode()
+    t = wl.to(dev)
+    B, Lc, k, H, c = wl.B, wl.Lc, wl.topk, wl.H, wl.c
+    out = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(api.sparse_attn_workspace_bytes(api.SA_OP_CSA_DECODE, B, wl.n_win, Lc, k, H, c),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.sparse_attn_csa_decode(t.q_idx, t.w, t.k_idx, None, t.n_comp, k, t.q, t.comp, t.win,
+                                   wl.sm_scale, out=out, lse=lse, idx_out=idx, ws=ws,
+                                   stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms = time_events(step, args.steps, stream)
+    qps = B / (ms * 1e-3)
+    # algorithmic bytes per query: index keys, index query and weights, the
+    # attended entries (selected + window), the core query and the output
+    ki = Lc * wl.dI * 2
+    qi = wl.HI * wl.dI * 2 + wl.HI * 4
+    gather = (k + wl.n_win) * c * 2
+    qm, o = H * c * 2, H * c * 4
+    per_q = ki + qi + gather + qm + o
+    step_frac = per_q * qps / (HBM_PEAK_GBS * 1e9)
+    log(f"{ms * 1e3:.1f} us/step, {qps:,.0f} queries/s, whole step {100 * step_frac:.1f}% of HBM peak")
+    if args.kernel_only:
+        return None
+    scores = torch.empty((B, 1, Lc), dtype=torch.float32, device=dev)
+
+    def idx_only():
+        api.sparse_attn_indexer_scores(t.q_idx[:, None], t.w[:, None], t.k_idx, scores=scores,
+                                       stream=stream)
+
+    idx_only()
+    idx_ms = timed_after(step, idx_only, max(5, min(args.steps, 50)), stream)
+    idx_bytes = B * (ki + qi)
+    idx_gbs = idx_bytes / (idx_ms * 1e-3) / 1e9
+    log(f"indexer over the entries {idx_ms * 1e3:.1f} us/launch, {idx_gbs:,.0f} GB/s algorithmic")
+    result = {
+        "metric": "compressed-entry selection decode queries/s (Lc=32K entries, k=2048, "
+                  "128-entry window)",
+        "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "Lc": Lc, "topk": k, "n_win": wl.n_win,
+                   "HI": wl.HI, "dI": wl.dI, "H": H, "c": c},
+        "hbm_frac_step": round(step_frac, 4), "bytes_per_query": per_q,
+        "roofline": {"bound": "hbm", "kernel": "indexer over the entries",
+                     "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us": round(idx_ms * 1e3, 2), "bytes_per_launch": idx_bytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.num_threads()
+        # whole sequences, 4 at a time, cycling over the batch until ~10 s
+        n, i = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            sl = slice(i, i + 4)
+            oracle.csa_decode(wl.q_idx[sl], wl.w[sl], wl.k_idx[sl], wl.q[sl], wl.comp[sl],
+                              wl.win[sl], k, wl.sm_scale)
+            n += 4
+            i = (i + 4) % B
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(n / dt, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} sequences of csa_decode, 4 at a time cycling over the {B} "
+                      f"(all {Lc} entries, all {H} heads each), fp64 oracle, {dt:.2f} s"}
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,7 +559,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_32k",
                     choices=["decode_32k", "decode_128k_fp8", "prefill_16k",
-                             "block_sparse_64k"])
+                             "block_sparse_64k", "csa_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-choice", action="store_true",
                     help="block_sparse_64k: one block choice per KV group (sum of its heads' "
@@ -500,6 +585,8 @@ def main():
         result = run_prefill(args, api, dev)
     elif args.workload == "block_sparse_64k":
         result = run_block(args, api, dev)
+    elif args.workload == "csa_decode":
+        result = run_csa(args, api, dev)
     else:
         result = run_decode(args, api, dev)
     if result is not None:

@@ -72,7 +72,8 @@ typedef enum {
   SA_OP_TOPK = 0,
   SA_OP_MLA_FORWARD = 1,
   SA_OP_DECODE = 2,
-  SA_OP_BLOCK_DECODE = 3
+  SA_OP_BLOCK_DECODE = 3,
+  SA_OP_CSA_DECODE = 4
 } sa_op;
 
 /* ---------------------------------------------------------------------------
@@ -178,6 +179,35 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w,
                        int dc, int dR, float sm_scale, float* out, float* lse,
                        int32_t* idx_out, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Selection over compressed entries (CSA-style decode step, T = 1).
+ *   "LLM注意力优化：稀疏注意力" DeepSeek CSA & HCA section: each m tokens of
+ *   KV cache are compressed into one entry (the compression is learned and is
+ *   the caller's); the indexer scores the query against the entries' index
+ *   keys, the top-k entries are kept, and core attention is MQA with the
+ *   selected entries as both keys and values; the most recent raw entries of a
+ *   sliding window are attended as well.  Reading: the window branch joins the
+ *   selected entries in one softmax (equal to merging the two branches'
+ *   outputs by log-sum-exp), a query head's output is
+ *     o_h = sum_{j in S U W} softmax_j(q_h . e_j * sm_scale) e_j.
+ *   Stages: indexer over the Lc entries' index keys (as sparse_attn_decode,
+ *   with n_comp[b] present entries, NULL = Lc), top-k, then the attention.
+ *   q [B, H, c] bf16; comp [B, Lc, c] bf16 entries; win [B, n_win, c] bf16
+ *   raw entries (may be NULL when n_win = 0); out [B, H, c] fp32; lse [B, H]
+ *   (may be NULL); idx_out [B, k] (may be NULL): the selected entries,
+ *   ascending, -1 padded.
+ * Compiled set: c = 512, H a multiple of 64; indexer and top-k as above.
+ * ws: sparse_attn_workspace_bytes(SA_OP_CSA_DECODE, B, n_win, Lc, k, H, c).
+ * ------------------------------------------------------------------------- */
+int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w,
+                           const void* k_idx, int k_dtype, const float* k_scale,
+                           const int32_t* n_comp, int B, int Lc, int HI, int dI,
+                           int k, const void* q, const void* comp,
+                           const void* win, int n_win, int H, int c,
+                           float sm_scale, float* out, float* lse,
+                           int32_t* idx_out, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* ---------------------------------------------------------------------------
  * Block-sparse variant: GQA decode over whole blocks.

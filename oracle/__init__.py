@@ -226,6 +226,45 @@ def masked_mla(q_lat, q_rope, kv, visible, sm_scale, dc=None, k_rope=None):
     return out, lse
 
 
+def csa_decode(q_idx, w, k_idx, q, comp, win, k, sm_scale, k_scale=None, n_comp=None,
+               allow_empty=False):
+    """Selection over compressed entries, one query per sequence
+    ("LLM注意力优化：稀疏注意力", DeepSeek CSA & HCA section):
+      1. index scores of the query against the Lc entries' index keys (the DSA
+         indexer, over n_comp[b] present entries);
+      2. the top-k entries by the DSA rule;
+      3. core attention as MQA with the entries as both keys and values, over
+         the selected entries and the n_win most recent raw entries (win),
+         one softmax over the union: o_h = sum_j softmax_j(q_h . e_j * scale) e_j.
+    q_idx [B,HI,dI], w [B,HI], k_idx [B,Lc,dI]; q [B,H,c]; comp [B,Lc,c];
+    win [B,n_win,c] or None.
+    -> (out[B,H,c], lse[B,H], idx[B,k] ascending -1 padded, count[B])"""
+    qi, wi = q_idx[:, None], w[:, None]
+    s = indexer(qi, wi, k_idx, k_scale=k_scale, kv_len=n_comp)
+    idx, cnt = topk(s, k, kv_len=n_comp)
+    out, lse = csa_attention(q, comp, win, _i32(idx)[:, 0], sm_scale, allow_empty=allow_empty)
+    return out, lse, _i32(idx)[:, 0], np.asarray(cnt)[:, 0]
+
+
+def csa_attention(q, comp, win, idx, sm_scale, allow_empty=False):
+    """Core attention of csa_decode given the selected entries idx[B,k]
+    (-1 = none): keys = values = entries, over the selected entries and every
+    window entry, one softmax.  -> (out[B,H,c], lse[B,H])"""
+    cd = decode(comp)
+    B, Lc, c = cd.shape
+    if win is not None and win.shape[1] > 0:
+        wd = decode(win)
+        rows = np.concatenate([cd, wd], axis=1)
+        n_win = wd.shape[1]
+    else:
+        rows, n_win = cd, 0
+    wslots = np.broadcast_to(Lc + np.arange(n_win, dtype=np.int32), (B, n_win))
+    full = np.concatenate([_i32(idx), wslots], axis=-1)[:, None]
+    out, lse = sparse_mla(decode(q)[:, None], None, rows, full, sm_scale, dc=c,
+                          allow_empty=allow_empty)
+    return out[:, 0], lse[:, 0]
+
+
 def block_pool(k, blk):
     """Mean-pooled block keys krep[B, L//blk, Hkv, d] over complete blocks."""
     kd = decode(k)

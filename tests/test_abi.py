@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     names = declared()
     for n in ("sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
               "sparse_attn_decode", "sparse_attn_workspace_bytes", "sparse_attn_status_string",
-              "sparse_attn_last_error", "sparse_attn_block_pool", "sparse_attn_block_decode"):
+              "sparse_attn_last_error", "sparse_attn_block_pool", "sparse_attn_block_decode",
+              "sparse_attn_csa_decode"):
         assert n in names
 
 

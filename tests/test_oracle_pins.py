@@ -593,3 +593,71 @@ def test_gqa_shared_choice_group_of_one_is_per_head(orc):
     o2, b2 = orc.block_sparse_decode(q, k, v, blk, 2, 1, 4, 0.5, shared=True)
     assert np.array_equal(b1, b2)
     np.testing.assert_array_equal(o1, o2)
+
+
+# --------------------------------------------------------------------------
+# selection over compressed entries (CSA-style): indexer + top-k over the
+# entries, MQA core attention with keys = values = entries, plus a window
+# --------------------------------------------------------------------------
+
+def _csa_inputs(seed, B=2, Lc=40, HI=3, dI=8, H=4, c=16, n_win=5):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g, dtype=torch.float64)
+    return (r(B, HI, dI), torch.rand(B, HI, generator=g, dtype=torch.float64), r(B, Lc, dI),
+            r(B, H, c), r(B, Lc, c), r(B, n_win, c) if n_win else None)
+
+
+def _softmax_attn(q, rows, scale):
+    # q [H,c], rows [n,c] (keys = values) -> out [H,c], lse [H]
+    z = q @ rows.T * scale
+    m = z.max(dim=1, keepdim=True).values
+    p = torch.exp(z - m)
+    return (p @ rows / p.sum(dim=1, keepdim=True)).numpy(), (m[:, 0] + torch.log(p.sum(dim=1))).numpy()
+
+
+def test_csa_all_entries_no_window_is_dense_mqa(orc):
+    # k >= Lc and no window: every entry is attended, keys = values
+    qi, w, ki, q, comp, _ = _csa_inputs(20, n_win=0)
+    out, lse, idx, cnt = orc.csa_decode(qi, w, ki, q, comp, None, 64, 0.25)
+    assert np.all(cnt == 40) and np.all(idx[:, :40] == np.arange(40)) and np.all(idx[:, 40:] == -1)
+    for b in range(2):
+        ro, rl = _softmax_attn(q[b], comp[b], 0.25)
+        np.testing.assert_allclose(out[b], ro, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-12, atol=1e-12)
+
+
+def test_csa_union_is_the_log_sum_exp_merge_of_both_branches(orc):
+    # one softmax over selected entries and window entries equals merging the
+    # two branches' outputs by their log-sum-exp weights
+    qi, w, ki, q, comp, win = _csa_inputs(21)
+    k = 7
+    out, lse, idx, cnt = orc.csa_decode(qi, w, ki, q, comp, win, k, 0.3)
+    for b in range(2):
+        sel = comp[b][torch.as_tensor(idx[b, :cnt[b]], dtype=torch.long)]
+        os_, ls = _softmax_attn(q[b], sel, 0.3)
+        ow, lw = _softmax_attn(q[b], win[b], 0.3)
+        a, c2 = np.exp(ls - np.maximum(ls, lw)), np.exp(lw - np.maximum(ls, lw))
+        merged = (a[:, None] * os_ + c2[:, None] * ow) / (a + c2)[:, None]
+        np.testing.assert_allclose(out[b], merged, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse[b], np.maximum(ls, lw) + np.log(a + c2), rtol=1e-12)
+
+
+def test_csa_selection_is_the_indexer_top_k(orc):
+    # the selected entries are the k highest index scores (brute force), and an
+    # entry outside the selection and the window does not move the output
+    qi, w, ki, q, comp, win = _csa_inputs(22)
+    k = 6
+    out, _, idx, cnt = orc.csa_decode(qi, w, ki, q, comp, win, k, 0.3)
+    for b in range(2):
+        sc = [sum(float(w[b, h]) * max(0.0, float(qi[b, h] @ ki[b, s])) for h in range(3))
+              for s in range(40)]
+        assert sorted(idx[b, :k].tolist()) == sorted(sorted(range(40), key=lambda s: (-sc[s], s))[:k])
+    unsel = [s for s in range(40) if s not in idx[1, :k]][0]
+    comp2 = comp.clone()
+    comp2[1, unsel] += 5.0
+    out2, _, _, _ = orc.csa_decode(qi, w, ki, q, comp2, win, k, 0.3)
+    np.testing.assert_array_equal(out2, out)
+    win2 = win.clone()
+    win2[1, 0] += 1.0
+    out3, _, _, _ = orc.csa_decode(qi, w, ki, q, comp, win2, k, 0.3)
+    assert np.abs(out3[1] - out[1]).max() > 1e-3 and np.array_equal(out3[0], out[0])

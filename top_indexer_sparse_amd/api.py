@@ -18,14 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 
 SA_OK = 0
 SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
-SA_OP_TOPK, SA_OP_MLA_FORWARD, SA_OP_DECODE, SA_OP_BLOCK_DECODE = 0, 1, 2, 3
+SA_OP_TOPK, SA_OP_MLA_FORWARD, SA_OP_DECODE, SA_OP_BLOCK_DECODE, SA_OP_CSA_DECODE = 0, 1, 2, 3, 4
 
 _DTYPE = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
 
 EXPORTS = (
     "sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
     "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode",
-    "sparse_attn_workspace_bytes", "sparse_attn_status_string", "sparse_attn_last_error",
+    "sparse_attn_csa_decode", "sparse_attn_workspace_bytes", "sparse_attn_status_string", "sparse_attn_last_error",
 )
 
 _lib = None
@@ -60,6 +60,8 @@ def load():
     L.sparse_attn_block_pool.argtypes = [P, I, I, I, I, I, P, P]
     L.sparse_attn_block_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
                                            P, P, SZ, P]
+    L.sparse_attn_csa_decode.argtypes = [P, I, P, P, I, P, P, I, I, I, I, I, P, P, P, I, I, I, F,
+                                         P, P, P, P, SZ, P]
     L.sparse_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.sparse_attn_workspace_bytes.restype = SZ
     L.sparse_attn_status_string.argtypes = [I]
@@ -67,7 +69,8 @@ def load():
     L.sparse_attn_last_error.argtypes = []
     L.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
-              "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode"):
+              "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode",
+              "sparse_attn_csa_decode"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -250,6 +253,44 @@ def sparse_attn_decode(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_
           _DTYPE[k_idx.dtype], _ptr(k_scale), _ptr(kv_len), B, L, HI, dI, topk, _ptr(q_lat),
           _ptr(q_rope), _DTYPE[dt], _ptr(c_kv), _ptr(k_rope), _DTYPE[dt], cs, rs, H, dc, dR,
           float(sm_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), nb, _stream(stream))
+    return out, lse, idx_out
+
+
+def sparse_attn_csa_decode(q_idx, w, k_idx, k_scale, n_comp, topk, q, comp, win, sm_scale,
+                           out=None, lse=None, idx_out=None, ws=None, stream=None):
+    """Selection over compressed entries (T = 1) -> (out [B,H,c], lse [B,H], idx [B,k]).
+
+    q_idx [B,HI,dI], w [B,HI], k_idx [B,Lc,dI] (+ k_scale [B,Lc] for fp8): the
+    indexer over the entries' index keys; q [B,H,c] bf16; comp [B,Lc,c] bf16
+    entries; win [B,n_win,c] bf16 raw window entries or None."""
+    B, HI, dI = q_idx.shape
+    Lc = k_idx.shape[1]
+    _, H, c = q.shape
+    n_win = 0 if win is None else win.shape[1]
+    _need(q_idx, "q_idx", (torch.float32, torch.bfloat16))
+    _need(w, "w", (torch.float32,), (B, HI))
+    _need(k_idx, "k_idx", (torch.float32, torch.bfloat16, torch.float8_e4m3fn), (B, Lc, dI))
+    _need(k_scale, "k_scale", (torch.float32,), (B, Lc), optional=True)
+    _need(n_comp, "n_comp", (torch.int32,), (B,), optional=True)
+    _need(q, "q", (torch.bfloat16,), (B, H, c))
+    _need(comp, "comp", (torch.bfloat16,), (B, Lc, c))
+    _need(win, "win", (torch.bfloat16,), (B, n_win, c), optional=True)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, c), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if idx_out is None:
+        idx_out = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.float32,), (B, H, c))
+    _need(lse, "lse", (torch.float32,), (B, H))
+    _need(idx_out, "idx_out", (torch.int32,), (B, topk))
+    ws, nb = _workspace(ws, sparse_attn_workspace_bytes(SA_OP_CSA_DECODE, B, n_win, Lc, topk, H, c),
+                        dev)
+    _call("sparse_attn_csa_decode", _ptr(q_idx), _DTYPE[q_idx.dtype], _ptr(w), _ptr(k_idx),
+          _DTYPE[k_idx.dtype], _ptr(k_scale), _ptr(n_comp), B, Lc, HI, dI, topk, _ptr(q),
+          _ptr(comp), _ptr(win), n_win, H, c, float(sm_scale), _ptr(out), _ptr(lse),
+          _ptr(idx_out), _ptr(ws), nb, _stream(stream))
     return out, lse, idx_out
 
 

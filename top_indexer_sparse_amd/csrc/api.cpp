@@ -102,7 +102,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct DecodeWs {
   size_t scores, idx, count, topk, mla, total;
 };
-DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype) {
+// n_win window slots follow the k index slots in the attention stage
+DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype, int n_win = 0) {
   DecodeWs w{};
   size_t off = 0;
   w.scores = off;
@@ -114,7 +115,7 @@ DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype) {
   w.topk = off;
   off = align256(off + sa::topk_workspace_bytes(B, 1, L, k));
   w.mla = off;
-  off = align256(off + sa::mla_workspace_bytes(kv_dtype, B, 1, k, H, dc));
+  off = align256(off + sa::mla_workspace_bytes(kv_dtype, B, 1, k + n_win, H, dc));
   w.total = off;
   return w;
 }
@@ -190,6 +191,51 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w, const
   return s;
 }
 
+int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w, const void* k_idx,
+                           int k_dtype, const float* k_scale, const int32_t* n_comp, int B, int Lc,
+                           int HI, int dI, int k, const void* q, const void* comp, const void* win,
+                           int n_win, int H, int c, float sm_scale, float* out, float* lse,
+                           int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  REQUIRE(q && comp && out, SA_ERR_NULL, "csa_decode: q, comp and out are required");
+  REQUIRE(n_win >= 0 && (n_win == 0 || win), SA_ERR_NULL, "csa_decode: win is required when n_win > 0");
+  REQUIRE(c == 512 && H >= 64 && H % 64 == 0, SA_ERR_UNSUPPORTED,
+          "csa_decode: c=%d, H=%d outside the compiled set (c = 512, H a multiple of 64)", c, H);
+  REQUIRE(aligned16(win), SA_ERR_ALIGN, "csa_decode: win must be 16-byte aligned");
+  if (!ws) return fail(SA_ERR_WORKSPACE, "csa_decode: a workspace is required");
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "csa_decode: workspace must be 16-byte aligned");
+  const DecodeWs lay = decode_ws(B < 0 ? 0 : B, Lc < 0 ? 0 : Lc, k < 1 ? 1 : k, H, c, SA_BF16, n_win);
+  char* base = (char*)ws;
+  float* scores = (float*)(base + lay.scores);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + lay.idx);
+  int32_t* count = (int32_t*)(base + lay.count);
+  sa::IndexerArgs ia{q_idx, q_idx_dtype, w, k_idx, k_dtype, k_scale, nullptr, n_comp, B, 1, Lc, HI, dI, scores};
+  sa::TopkArgs ta{scores, nullptr, n_comp, B, 1, Lc, k, idx, count, base + lay.topk};
+  // keys = values = entries: the latent part is the entry, the RoPE part is absent
+  sa::MlaArgs ma{q, nullptr, SA_BF16, comp, nullptr, c, 0, idx, k, B, 1, Lc, H, c, 64,
+                 sm_scale, out, lse, base + lay.mla};
+  ma.win = win;
+  ma.win_stride = c;
+  ma.n_win = n_win;
+  ma.zero_rope = 1;
+  int s = check_indexer(ia);
+  if (s == SA_OK) s = check_topk(ta, lay.mla - lay.topk);
+  if (s == SA_OK) {
+    REQUIRE(sa::mla_supported(ma), SA_ERR_UNSUPPORTED, "csa_decode: entries beyond 4 GiB per sequence");
+    REQUIRE(aligned16(q) && aligned16(comp) && aligned16(out) && aligned16(lse) && aligned16(idx_out),
+            SA_ERR_ALIGN, "csa_decode: pointers must be 16-byte aligned");
+    if (ws_bytes < lay.total)
+      s = fail(SA_ERR_WORKSPACE, "csa_decode: workspace of %zu bytes required, %zu given", lay.total,
+               ws_bytes);
+  }
+  if (s != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  s = hip_status(sa::launch_indexer(ia, st), "csa indexer launch");
+  if (s == SA_OK) s = hip_status(sa::launch_topk(ta, st), "csa topk launch");
+  if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "csa attention launch");
+  return s;
+}
+
 int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, float* krep,
                            void* stream) {
   clear_error();
@@ -234,6 +280,8 @@ size_t sparse_attn_workspace_bytes(int op, int B, int T, int L, int k, int H, in
       return decode_ws(B, L, k, H, dc, SA_BF16).total;
     case SA_OP_BLOCK_DECODE:  // (B, Hq, L, nsel, Hkv, d) passed as (B, T, L, k, H, dc)
       return sa::block_workspace_bytes(B, T, L, k, H, dc, 32);
+    case SA_OP_CSA_DECODE:  // (B, n_win, Lc, k, H, c) passed as (B, T, L, k, H, dc)
+      return decode_ws(B, L, k, H, dc, SA_BF16, T).total;
   }
   return 0;
 }

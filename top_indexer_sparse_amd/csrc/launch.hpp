@@ -51,6 +51,13 @@ struct MlaArgs {
   float* out;
   float* lse;
   void* ws;
+  // Optional (bf16 MFMA path): a second row source of n_win rows, reached by
+  // n_win extra slots after the k index slots (slot k + i reads win row i),
+  // and zero_rope = 1 for rows without a RoPE part (q_rope, k_rope unused).
+  const void* win = nullptr;
+  int64_t win_stride = 0;  // elements
+  int n_win = 0;
+  int zero_rope = 0;
 };
 bool mla_uses_mfma(const MlaArgs& a);
 bool mla_supported(const MlaArgs& a);

@@ -89,7 +89,14 @@ struct MlaKernelArgs {
   float* lse;              // [BT, H] or null
   float* part_o;           // [BT, H, nsplit, 512] when nsplit > 1
   float* part_ml;          // [BT, H, nsplit, 2]
+  const uint8_t* win;      // row i of sequence b at + (b*n_win+i)*win_stride_b
+  int64_t win_stride_b;
+  int n_win;               // slots k .. k+n_win-1 read win rows 0 .. n_win-1
+  int zero_rope;           // no RoPE part: q_rope and k_rope read as zeros
 };
+
+// 128 zero bytes: the RoPE operand of rows that have none.
+__device__ __attribute__((aligned(256))) uint8_t g_mla_zero[128];
 
 // NW waves; one work-group per (query, head group, KV split).  Each wave owns
 // 16 heads and 512 / DS of the output dims: with DS = 2, the two waves of a
@@ -123,7 +130,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   const int h = hg * HW + hb * 16 + n;       // this lane's head
 
   const int j_begin = split * a.slots_per_split;
-  const int nslots = max(0, min(a.k, j_begin + a.slots_per_split) - j_begin);
+  const int kt = a.k + a.n_win;  // index slots, then window slots
+  const int nslots = max(0, min(kt, j_begin + a.slots_per_split) - j_begin);
+  const uint32_t nrows = (uint32_t)(a.L + a.n_win);  // valid slot values
   const int32_t* idxr = a.idx + bt * a.k + j_begin;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tiles[0][0];
@@ -149,7 +158,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   constexpr int kQRuns = NH * 18 / NW;  // 1 KB query runs per wave
   {
     const uint8_t* qlb = uniform_ptr((const uint8_t*)(a.q_lat + (bt * a.H + (int64_t)hg * HW) * kMlaDc));
-    const uint8_t* qrb = uniform_ptr((const uint8_t*)(a.q_rope + (bt * a.H + (int64_t)hg * HW) * kMlaDr));
+    const uint8_t* qrb =
+        a.zero_rope ? g_mla_zero
+                    : uniform_ptr((const uint8_t*)(a.q_rope + (bt * a.H + (int64_t)hg * HW) * kMlaDr));
+    const uint32_t qr_head = a.zero_rope ? 0u : 2u * kMlaDr;  // zero rows: one 128-byte row
     const int qn = lane >> 2, qg = lane & 3;
 #pragma unroll
     for (int i = 0; i < kQRuns; ++i) {
@@ -160,11 +172,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
       if (ks < 16)
         dma16(qlb, head * (2u * kMlaDc) + 64u * ks + 16u * qg, dst);
       else
-        dma16(qrb, head * (2u * kMlaDr) + 64u * (ks - 16) + 16u * qg, dst);
+        dma16(qrb, head * qr_head + 64u * (ks - 16) + 16u * qg, dst);
     }
   }
   wait_vmcnt<kQRuns>();  // this wave's index slice landed (the query runs may not)
   lds_barrier();         // every wave's slice landed
+  if (a.n_win > 0 && j_begin + nslots > a.k) {  // window slots: positions L, L+1, ...
+    for (int j = max(0, a.k - j_begin) + tid; j < nslots; j += 64 * NW) spos[j] = a.L + j_begin + j - a.k;
+    wait_lgkm0();
+    lds_barrier();
+  }
   // Every slot of the slice is processed; a slot that holds no position in
   // [0, L) fetches row 0 and is masked out of the softmax.
   const int ntiles = (nslots + kMlaTile - 1) / kMlaTile;
@@ -180,6 +197,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   constexpr int NLD = kMlaTileLoads / NH;  // loads per tile and issuing wave
   const uint8_t* cb = a.c_kv + (int64_t)b * a.L * a.c_stride_b;
   const uint8_t* rb = a.k_rope + (int64_t)b * a.L * a.r_stride_b;
+  const uint8_t* wb = a.win + (int64_t)b * a.n_win * a.win_stride_b;
   const int wv = __builtin_amdgcn_readfirstlane(hb);
   const bool issuer = __builtin_amdgcn_readfirstlane(dh) == 0;
   uint32_t drow[NLD], dpiece[NLD];
@@ -206,15 +224,21 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     for (int i = I0; i < I1; ++i) srow[i] = *(const uint32_t*)(sp + drow[i]);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-      const uint32_t s = srow[i] < (uint32_t)a.L ? srow[i] : 0u;  // skipped slot: row 0
+      const uint32_t s = srow[i] < nrows ? srow[i] : 0u;  // skipped slot: row 0
       const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NH * i);
       if constexpr (PACKED) {
         dma16(cb, s * (uint32_t)a.c_stride_b + dpiece[i], ldst);
       } else {
         const bool rope = dpiece[i] >= 1024u;
-        const uint8_t* base = rope ? rb : cb;
-        const uint32_t stride = rope ? (uint32_t)a.r_stride_b : (uint32_t)a.c_stride_b;
-        dma16_addr(base + (s * stride + (dpiece[i] & 1023u)), ldst);
+        const uint8_t* src;
+        if (rope)
+          src = a.zero_rope ? g_mla_zero + (dpiece[i] & 1023u)
+                            : rb + (s * (uint32_t)a.r_stride_b + (dpiece[i] & 1023u));
+        else if (s < (uint32_t)a.L)
+          src = cb + (s * (uint32_t)a.c_stride_b + dpiece[i]);
+        else
+          src = wb + ((s - (uint32_t)a.L) * (uint32_t)a.win_stride_b + dpiece[i]);
+        dma16_addr(src, ldst);
       }
     }
   };
@@ -236,7 +260,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     const int j0 = 64 * NW * i;
     if (j0 >= ntiles * kMlaTile) break;  // uniform
     const int j = j0 + tid;
-    const bool ok = j < nslots && (uint32_t)spos[j] < (uint32_t)a.L;
+    const bool ok = j < nslots && (uint32_t)spos[j] < nrows;
     const uint64_t m = __ballot(ok);  // 64 slots = two tiles
     const int t0 = j0 / kMlaTile + 2 * wave;  // this wave's first tile
     if (lane == 0 && t0 < ntiles) {
@@ -673,7 +697,9 @@ bool mla_uses_mfma(const MlaArgs& a) {
 bool mla_supported(const MlaArgs& a) {
   // the bf16 path addresses a sequence's rows with 32-bit byte offsets
   if (mla_uses_mfma(a))
-    return (int64_t)a.L * a.c_stride * 2 < (1LL << 32) && (int64_t)a.L * a.r_stride * 2 < (1LL << 32);
+    return (int64_t)a.L * a.c_stride * 2 < (1LL << 32) && (int64_t)a.L * a.r_stride * 2 < (1LL << 32) &&
+           (int64_t)a.n_win * a.win_stride * 2 < (1LL << 32) && (a.n_win == 0 || a.zero_rope);
+  if (a.n_win || a.zero_rope) return false;  // window rows and RoPE-free rows: bf16 MFMA path only
   if (a.dc > 512 || a.dR > 64 || a.dR < 0 || a.dc < 1) return false;
   if ((int64_t)a.H * a.dc > 256 * kVecMaxOut) return false;
   return vector_lds_bytes(a.H, a.dc, a.dR) <= 64 * 1024;
@@ -709,15 +735,20 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
     m.k_rope = (const uint8_t*)a.k_rope;
     m.c_stride_b = a.c_stride * 2;
     m.r_stride_b = a.r_stride * 2;
-    m.packed = a.c_stride == a.r_stride &&
+    m.packed = a.c_stride == a.r_stride && !a.zero_rope && a.n_win == 0 &&
                (const uint8_t*)a.k_rope == (const uint8_t*)a.c_kv + 2 * kMlaDc;
+    m.win = (const uint8_t*)a.win;
+    m.win_stride_b = a.win_stride * 2;
+    m.n_win = a.n_win;
+    m.zero_rope = a.zero_rope;
+    const int kt = a.k + a.n_win;  // slots: the index set, then the window
     m.idx = a.idx;
     m.k = a.k;
     m.T = a.T;
     m.L = a.L;
     m.H = a.H;
-    m.nsplit = mla_nsplit(bt, a.H, a.k);
-    m.slots_per_split = ((a.k + m.nsplit - 1) / m.nsplit + kMlaTile - 1) / kMlaTile * kMlaTile;
+    m.nsplit = mla_nsplit(bt, a.H, kt);
+    m.slots_per_split = ((kt + m.nsplit - 1) / m.nsplit + kMlaTile - 1) / kMlaTile * kMlaTile;
     m.scale_log2 = scale_log2;
     m.out = a.out;
     m.lse = a.lse;

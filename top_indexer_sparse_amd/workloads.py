@@ -272,3 +272,60 @@ def block_sparse_64k(B: int = 16, L: int = 65536, Hq: int = 32, Hkv: int = 8,
     v = _randn((B, L, Hkv, d), wid, 2).to(torch.bfloat16)
     return BlockWorkload("block_sparse_64k", B, L, Hq, Hkv, d, blk, nsel,
                          n_sink, n_win, 1.0 / math.sqrt(d), q, k, v)
+
+
+W_CSA_DECODE = 6
+
+
+@dataclass
+class CsaWorkload:
+    """Selection over compressed entries, one query per sequence.
+
+    q_idx [B,HI,dI] bf16, w [B,HI] fp32, k_idx [B,Lc,dI] bf16: the indexer over
+    the entries' index keys; q [B,H,c] bf16; comp [B,Lc,c] bf16 compressed
+    entries (keys = values); win [B,n_win,c] bf16 the most recent raw entries;
+    n_comp [B] int32 entries present (None: Lc)."""
+    name: str
+    B: int
+    Lc: int
+    HI: int
+    dI: int
+    topk: int
+    H: int
+    c: int
+    n_win: int
+    sm_scale: float
+    q_idx: torch.Tensor
+    w: torch.Tensor
+    k_idx: torch.Tensor
+    q: torch.Tensor
+    comp: torch.Tensor
+    win: Optional[torch.Tensor]
+    n_comp: Optional[torch.Tensor] = None
+
+    def to(self, device):
+        out = CsaWorkload(**{**self.__dict__})
+        for f in ("q_idx", "w", "k_idx", "q", "comp", "win", "n_comp"):
+            v = getattr(self, f)
+            if v is not None:
+                setattr(out, f, v.to(device))
+        return out
+
+
+def csa_decode(B: int = 32, Lc: int = 32768, HI: int = 64, dI: int = 128,
+               topk: int = 2048, H: int = 128, c: int = 512, n_win: int = 128,
+               n_comp=None, wid: int = W_CSA_DECODE) -> CsaWorkload:
+    """Decode over Lc = n/m compressed entries (a 131072-token context at
+    m = 4 by default) plus a window of the n_win most recent raw entries.
+    The entries are synthetic N(0,1): the learned compression is the caller's."""
+    q_idx = _randn((B, HI, dI), wid, 0).to(torch.bfloat16)
+    w = _rand((B, HI), wid, 1)
+    k_idx = _randn((B, Lc, dI), wid, 2).to(torch.bfloat16)
+    q = _randn((B, H, c), wid, 3).to(torch.bfloat16)
+    comp = _randn((B, Lc, c), wid, 4).to(torch.bfloat16)
+    win = _randn((B, n_win, c), wid, 5).to(torch.bfloat16) if n_win else None
+    nc = None
+    if n_comp is not None:
+        nc = torch.as_tensor(n_comp, dtype=torch.int32).reshape(B).contiguous()
+    return CsaWorkload("csa_decode", B, Lc, HI, dI, topk, H, c, n_win,
+                       1.0 / math.sqrt(c), q_idx, w, k_idx, q, comp, win, nc)
