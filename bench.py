@@ -20,8 +20,9 @@ The JSON line carries, besides the contract fields:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W]
-       [--workload decode_32k|decode_128k_fp8|prefill_16k|block_sparse_64k]
-       [--no-cpu-baseline] [--kernel-only]
+       [--workload decode_32k|decode_128k_fp8|prefill_16k|block_sparse_64k|csa_decode|
+                   prefill_crossover]
+       [--staged] [--shared-choice] [--no-cpu-baseline] [--kernel-only]
 """
 import argparse
 import json
@@ -271,9 +272,17 @@ def prefill_indexer_flop(wl):
     return pairs * 2 * wl.HI * wl.dI
 
 
+def prefill_mla_flop(wl, rows):
+    """Flops of the sparse MLA over `rows` gathered rows summed over queries:
+    per row and head, 2 (d_c + d_R) for the score and 2 d_c for the value."""
+    return rows * wl.H * 2 * (2 * wl.dc + wl.dR)
+
+
 def run_prefill(args, api, dev):
-    """Causal prefill, T = L = 16384: indexer (MFMA contraction with the causal
-    mask) -> top-k per query row -> sparse MLA for every query."""
+    """Causal prefill, T = L = 16384, through sparse_attn_prefill (sparse mode):
+    the fused select (indexer scores and Top-K per query row, the row held on
+    chip, no [T, L] score tensor), then the sparse MLA for every query.
+    --staged times the three-call path instead (score tensor, top-k, MLA)."""
     import torch
     from top_indexer_sparse_amd import workloads
     log("generating prefill_16k")
@@ -281,28 +290,42 @@ def run_prefill(args, api, dev):
     t = wl.to(dev)
     T, L, k = wl.T, wl.L, wl.topk
     c_kv, k_rope = t.kv[..., :wl.dc], t.kv[..., wl.dc:]
-    scores = torch.empty((1, T, L), dtype=torch.float32, device=dev)
     idx = torch.empty((1, T, k), dtype=torch.int32, device=dev)
     cnt = torch.empty((1, T), dtype=torch.int32, device=dev)
     out = torch.empty((1, T, wl.H, wl.dc), dtype=torch.float32, device=dev)
     lse = torch.empty((1, T, wl.H), dtype=torch.float32, device=dev)
-    tws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_TOPK, 1, T, L, k, 0, 0)),
-                      dtype=torch.uint8, device=dev)
-    mws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_MLA_FORWARD, 1, T, L, k,
-                                                              wl.H, wl.dc)),
-                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.staged:
+        scores = torch.empty((1, T, L), dtype=torch.float32, device=dev)
+        tws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_TOPK, 1, T, L, k, 0, 0)),
+                          dtype=torch.uint8, device=dev)
+        mws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_MLA_FORWARD, 1, T, L, k,
+                                                                  wl.H, wl.dc)),
+                          dtype=torch.uint8, device=dev)
 
-    def indexer():
-        api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, q_pos=t.q_pos, scores=scores,
-                                       stream=stream)
+        def select():
+            api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, q_pos=t.q_pos, scores=scores,
+                                           stream=stream)
+            api.sparse_attn_topk(scores, k, q_pos=t.q_pos, idx=idx, count=cnt, ws=tws,
+                                 stream=stream)
 
-    def step():
-        indexer()
-        api.sparse_attn_topk(scores, k, q_pos=t.q_pos, idx=idx, count=cnt, ws=tws,
-                             stream=stream)
-        api.sparse_attn_mla_forward(t.q_lat, t.q_rope, c_kv, k_rope, idx, wl.sm_scale,
-                                    out=out, lse=lse, ws=mws, stream=stream)
+        def step():
+            select()
+            api.sparse_attn_mla_forward(t.q_lat, t.q_rope, c_kv, k_rope, idx, wl.sm_scale,
+                                        out=out, lse=lse, ws=mws, stream=stream)
+    else:
+        ws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_PREFILL, 1, T, L, k,
+                                                                 wl.H, wl.dc)),
+                         dtype=torch.uint8, device=dev)
+
+        def select():
+            api.sparse_attn_prefill_select(t.q_idx, t.w, t.k_idx, k, q_pos=t.q_pos, idx=idx,
+                                           count=cnt, stream=stream)
+
+        def step():
+            api.sparse_attn_prefill(t.q_idx, t.w, t.k_idx, k, t.q_lat, t.q_rope, c_kv, k_rope,
+                                    wl.sm_scale, q_pos=t.q_pos, mode=api.SA_PREFILL_SPARSE,
+                                    out=out, lse=lse, idx_out=idx, ws=ws, stream=stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -311,16 +334,21 @@ def run_prefill(args, api, dev):
     log(f"timing {args.steps} steps")
     ms = time_events(step, args.steps, stream)
     qps = T / (ms * 1e-3)
-    log(f"{ms:.2f} ms/step, {qps:,.0f} queries/s")
+    log(f"{ms:.2f} ms/step, {qps:,.0f} queries/s ({'staged' if args.staged else 'fused select'})")
     if args.kernel_only:
         return None
-    idx_ms = timed_after(step, indexer, max(3, min(args.steps, 10)), stream)
+    sel_ms = timed_after(step, select, max(3, min(args.steps, 10)), stream)
     flop = prefill_indexer_flop(wl)
-    tfs = flop / (idx_ms * 1e-3) / 1e12
-    log(f"indexer {idx_ms:.3f} ms, {tfs:,.0f} TFLOP/s = {100 * tfs / BF16_PEAK_TFLOPS:.1f}% "
-        f"of bf16 MFMA peak")
+    tfs = flop / (sel_ms * 1e-3) / 1e12
+    what = "indexer scores + top-k" if args.staged else "fused select (scores + top-k)"
+    log(f"{what} {sel_ms:.3f} ms: indexer flops at {tfs:,.0f} TFLOP/s = "
+        f"{100 * tfs / BF16_PEAK_TFLOPS:.1f}% of bf16 MFMA peak")
+    rows = int(torch.clamp(cnt, max=k).sum().item())
+    mla_ms = ms - sel_ms
+    mla_tfs = prefill_mla_flop(wl, rows) / (mla_ms * 1e-3) / 1e12
+    log(f"sparse MLA ~{mla_ms:.2f} ms over {rows:,} rows: {mla_tfs:,.0f} TFLOP/s")
     result = {
-        "metric": "prefill queries/s at T=L=16K, k=2048; indexer % of bf16 MFMA peak",
+        "metric": "prefill queries/s at T=L=16K, k=2048; select % of bf16 MFMA peak",
         "value": round(qps, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -333,16 +361,67 @@ def run_prefill(args, api, dev):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": 1, "T": T, "L": L, "topk": k, "HI": wl.HI,
-                   "dI": wl.dI, "H": wl.H, "dc": wl.dc, "dR": wl.dR},
-        "roofline": {"bound": "mfma", "kernel": "indexer (causal QK^T)", "achieved": round(tfs, 1),
+                   "dI": wl.dI, "H": wl.H, "dc": wl.dc, "dR": wl.dR,
+                   "path": "staged" if args.staged else "fused_select"},
+        "roofline": {"bound": "mfma", "kernel": what, "achieved": round(tfs, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "launch_us": round(idx_ms * 1e3, 1), "flop_per_launch": flop},
+                     "launch_us": round(sel_ms * 1e3, 1), "flop_per_launch": flop},
+        "roofline_mla": {"bound": "mfma", "achieved": round(mla_tfs, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(mla_tfs / BF16_PEAK_TFLOPS, 4),
+                         "ms": round(mla_ms, 3), "rows": rows},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on a sample")
         result["cpu_baseline"] = cpu_baseline_prefill(wl)
     return result
+
+
+def run_crossover(args, api, dev):
+    """Dense (every causal candidate) against sparse (fused select + k rows)
+    prefill at T = L for L = 1K .. 16K, k = 2048, H = 128: the short-sequence
+    crossover of the two modes of sparse_attn_prefill."""
+    import torch
+    from top_indexer_sparse_amd import workloads
+    stream = torch.cuda.current_stream()
+    table = []
+    for L in (1024, 1536, 2048, 2560, 3072, 4096, 6144, 8192, 16384):
+        wl = workloads.prefill_16k(L=L, n_needles=0)
+        t = wl.to(dev)
+        c_kv, k_rope = t.kv[..., :wl.dc], t.kv[..., wl.dc:]
+        out = torch.empty((1, L, wl.H, wl.dc), dtype=torch.float32, device=dev)
+        lse = torch.empty((1, L, wl.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_PREFILL, 1, L, L,
+                                                                 wl.topk, wl.H, wl.dc)),
+                         dtype=torch.uint8, device=dev)
+        row = {"L": L}
+        for name, mode in (("sparse", api.SA_PREFILL_SPARSE), ("dense", api.SA_PREFILL_DENSE)):
+            def step():
+                api.sparse_attn_prefill(t.q_idx, t.w, t.k_idx, wl.topk, t.q_lat, t.q_rope, c_kv,
+                                        k_rope, wl.sm_scale, q_pos=t.q_pos, mode=mode, out=out,
+                                        lse=lse, ws=ws, stream=stream)
+            for _ in range(2):
+                step()
+            n = max(3, min(args.steps, 20 if L <= 4096 else 5))
+            row[f"{name}_ms"] = round(time_events(step, n, stream), 4)
+        row["dense_over_sparse"] = round(row["dense_ms"] / row["sparse_ms"], 3)
+        log(f"L={L:6d}: sparse {row['sparse_ms']:.3f} ms, dense {row['dense_ms']:.3f} ms "
+            f"(dense/sparse {row['dense_over_sparse']:.2f})")
+        table.append(row)
+        del t, out, lse, ws
+        torch.cuda.empty_cache()
+    faster = [r["L"] for r in table if r["dense_ms"] <= r["sparse_ms"]]
+    cross = max(faster) if faster else None
+    last = table[-1]
+    return {
+        "metric": "prefill dense/sparse crossover (T=L, k=2048): longest L where dense is faster",
+        "value": cross, "unit": "tokens", "n_gpus": 1, "steps": args.steps,
+        "warmup": 2, "ms_per_step": last["sparse_ms"], "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_crossover", "k": 2048, "H": 128, "HI": 64, "dI": 128},
+        "sweep": table,
+    }
 
 
 def cpu_baseline_prefill(wl, stride=64):
@@ -559,8 +638,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_32k",
                     choices=["decode_32k", "decode_128k_fp8", "prefill_16k",
-                             "block_sparse_64k", "csa_decode"])
+                             "block_sparse_64k", "csa_decode", "prefill_crossover"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--staged", action="store_true",
+                    help="prefill_16k: time the three-call path (score tensor, top-k, MLA) "
+                         "instead of the fused select")
     ap.add_argument("--shared-choice", action="store_true",
                     help="block_sparse_64k: one block choice per KV group (sum of its heads' "
                          "block scores)")
@@ -587,6 +669,8 @@ def main():
         result = run_block(args, api, dev)
     elif args.workload == "csa_decode":
         result = run_csa(args, api, dev)
+    elif args.workload == "prefill_crossover":
+        result = run_crossover(args, api, dev)
     else:
         result = run_decode(args, api, dev)
     if result is not None:

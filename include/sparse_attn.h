@@ -73,8 +73,16 @@ typedef enum {
   SA_OP_MLA_FORWARD = 1,
   SA_OP_DECODE = 2,
   SA_OP_BLOCK_DECODE = 3,
-  SA_OP_CSA_DECODE = 4
+  SA_OP_CSA_DECODE = 4,
+  SA_OP_PREFILL = 5
 } sa_op;
+
+/* Attention modes of sparse_attn_prefill. */
+typedef enum {
+  SA_PREFILL_SPARSE = 0, /* indexer -> Top-K -> MLA over the k selected rows  */
+  SA_PREFILL_DENSE = 1,  /* MLA over every causal candidate (MHA + mask)      */
+  SA_PREFILL_AUTO = 2    /* DENSE when L <= k, else SPARSE                    */
+} sa_prefill_mode;
 
 /* ---------------------------------------------------------------------------
  * Stage 1: lightning indexer scores.
@@ -179,6 +187,62 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w,
                        int dc, int dR, float sm_scale, float* out, float* lse,
                        int32_t* idx_out, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused prefill select: stages 1 and 2 in one kernel, with no [B, T, L] score
+ * tensor.  "MLA 与稀疏注意力" DSA section (I_{t,s}, then TopK over s <= t);
+ * "Sparse Attention 数学学习笔记" §9.  One work-group per query row computes
+ * the row's index scores into on-chip memory (4 bytes per position) and
+ * selects from them there; only idx and count are written.  The scores carry
+ * the same bits as sparse_attn_indexer_scores' for the same inputs, and the
+ * selection follows the rule of sparse_attn_topk, so idx and count equal
+ * what those two calls produce.
+ *   Arguments as sparse_attn_indexer_scores (q_idx [B,T,HI,dI], w [B,T,HI],
+ *   k_idx [B,L,dI], k_scale, q_pos, kv_len) and sparse_attn_topk (k, idx
+ *   [B,T,k] ascending and -1 padded, count [B,T] or NULL).
+ * Compiled set: q_dtype SA_BF16, k_dtype SA_BF16 or SA_FP8_E4M3, HI in
+ * {16, 32, 64, 128}, dI in {64, 128}, 1 <= L <= 32768, k >= 1.  No workspace.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_prefill_select(const void* q_idx, int q_dtype, const float* w,
+                               const void* k_idx, int k_dtype,
+                               const float* k_scale, const int32_t* q_pos,
+                               const int32_t* kv_len, int B, int T, int L,
+                               int HI, int dI, int k, int32_t* idx,
+                               int32_t* count, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefill: every query of a causal prefill, in one call.
+ *   mode SA_PREFILL_SPARSE: sparse_attn_prefill_select, then stage 3 over the
+ *     selected rows ("Sparse Attention 数学学习笔记" §8-§9).
+ *   mode SA_PREFILL_DENSE: stage 3 over every candidate position s <
+ *     min(q_pos[b,t] + 1, kv_len[b], L), with no indexer and no Top-K: the
+ *     dense attention with a causal mask that "LLM注意力优化：稀疏注意力" (DSA
+ *     section) names as the better choice for short sequences.  The result is
+ *     the sparse one whenever no row has more than k candidates.
+ *   mode SA_PREFILL_AUTO: DENSE when L <= k, else SPARSE.  With L <= k no row
+ *     has more than k candidates, so both modes attend to the same rows and
+ *     the dense one skips the indexer and the Top-K; above k the sparse mode
+ *     is the faster one on MI355X already from L = 1.5 k (k = 2048, H = 128:
+ *     1.27x at L = 3072, 1.64x at 4096, 5.6x at 16384), so the switch never
+ *     changes a result.
+ * Arguments as sparse_attn_prefill_select (the indexer inputs may be NULL in
+ * the dense mode) and sparse_attn_mla_forward (q_lat [B,T,H,dc], q_rope
+ * [B,T,H,dR], strided c_kv / k_rope rows).  idx_out [B,T,k] (may be NULL;
+ * sparse mode only) receives the selected sets.
+ * Compiled set: the prefill select's, and the bf16 MLA path ((dc, dR) =
+ * (512, 64), H a multiple of 64).
+ * ws: sparse_attn_workspace_bytes(SA_OP_PREFILL, B, T, L, k, H, dc), which
+ * covers every mode.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_prefill(const void* q_idx, int q_idx_dtype, const float* w,
+                        const void* k_idx, int k_dtype, const float* k_scale,
+                        const int32_t* q_pos, const int32_t* kv_len, int B,
+                        int T, int L, int HI, int dI, int k, const void* q_lat,
+                        const void* q_rope, const void* c_kv,
+                        const void* k_rope, int64_t c_stride, int64_t r_stride,
+                        int H, int dc, int dR, float sm_scale, int mode,
+                        float* out, float* lse, int32_t* idx_out, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Selection over compressed entries (CSA-style decode step, T = 1).

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     for n in ("sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
               "sparse_attn_decode", "sparse_attn_workspace_bytes", "sparse_attn_status_string",
               "sparse_attn_last_error", "sparse_attn_block_pool", "sparse_attn_block_decode",
-              "sparse_attn_csa_decode"):
+              "sparse_attn_csa_decode", "sparse_attn_prefill_select", "sparse_attn_prefill"):
         assert n in names
 
 
@@ -142,3 +142,36 @@ def test_block_validation(lib):
     pool = lib.sparse_attn_block_pool
     assert pool(A, 1, 4096, 2, 128, 48, A, None) == 5  # block size not compiled
     assert pool(None, 1, 4096, 2, 128, 64, A, None) == 1
+
+
+def test_prefill_select_validation(lib):
+    f = lib.sparse_attn_prefill_select
+    # fp32 queries run only on the vector score path: not fused
+    assert f(A, 0, A, A, 1, None, A, None, 1, 16, 4096, 64, 128, 64, A, None, None) == 5
+    # the row must fit on chip
+    assert f(A, 1, A, A, 1, None, A, None, 1, 16, 40000, 64, 128, 64, A, None, None) == 5
+    assert "L <= 32768" in _err(lib)
+    assert f(A, 1, A, A, 1, None, A, None, 1, 16, 4096, 64, 128, 0, A, None, None) == 2
+    assert f(A, 1, A, A, 1, None, A, None, 1, 16, 4096, 64, 128, 64, None, None, None) == 1
+    assert f(A, 1, A, A, 1, None, A, None, 1, 16, 4096, 64, 128, 64, A, M, None) == 4
+
+
+def test_prefill_validation(lib):
+    f = lib.sparse_attn_prefill
+    F = ctypes.c_float(0.1)
+    idx_args = [A, 1, A, A, 1, None, A, None, 1, 1024, 4096, 64, 128, 2048]
+    mla_args = [A, A, A, A, 576, 576, 128, 512, 64, F]
+    need = lib.sparse_attn_workspace_bytes(5, 1, 1024, 4096, 2048, 128, 512)
+    assert need >= 1024 * 2048 * 4
+    # unknown mode
+    assert f(*idx_args, *mla_args, 3, A, None, None, A, need, None) == 2
+    # no workspace, short workspace
+    assert f(*idx_args, *mla_args, 0, A, None, None, None, 0, None) == 6
+    assert f(*idx_args, *mla_args, 1, A, None, None, A, need - 256, None) == 6
+    # the dense mode needs no indexer inputs, but still the bf16 attention shapes
+    bad_h = [A, A, A, A, 576, 576, 100, 512, 64, F]
+    assert f(None, 1, None, None, 1, None, A, None, 1, 1024, 4096, 0, 0, 2048, *bad_h, 1, A, None,
+             None, A, need, None) == 5
+    # the sparse mode needs them
+    assert f(None, 1, None, None, 1, None, A, None, 1, 1024, 4096, 0, 0, 2048, *mla_args, 0, A,
+             None, None, A, need, None) == 1

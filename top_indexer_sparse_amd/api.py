@@ -19,13 +19,16 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 SA_OK = 0
 SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
 SA_OP_TOPK, SA_OP_MLA_FORWARD, SA_OP_DECODE, SA_OP_BLOCK_DECODE, SA_OP_CSA_DECODE = 0, 1, 2, 3, 4
+SA_OP_PREFILL = 5
+SA_PREFILL_SPARSE, SA_PREFILL_DENSE, SA_PREFILL_AUTO = 0, 1, 2
 
 _DTYPE = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
 
 EXPORTS = (
     "sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
     "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode",
-    "sparse_attn_csa_decode", "sparse_attn_workspace_bytes", "sparse_attn_status_string", "sparse_attn_last_error",
+    "sparse_attn_csa_decode", "sparse_attn_prefill_select", "sparse_attn_prefill",
+    "sparse_attn_workspace_bytes", "sparse_attn_status_string", "sparse_attn_last_error",
 )
 
 _lib = None
@@ -62,6 +65,9 @@ def load():
                                            P, P, SZ, P]
     L.sparse_attn_csa_decode.argtypes = [P, I, P, P, I, P, P, I, I, I, I, I, P, P, P, I, I, I, F,
                                          P, P, P, P, SZ, P]
+    L.sparse_attn_prefill_select.argtypes = [P, I, P, P, I, P, P, P, I, I, I, I, I, I, P, P, P]
+    L.sparse_attn_prefill.argtypes = [P, I, P, P, I, P, P, P, I, I, I, I, I, I, P, P, P, P, I64,
+                                      I64, I, I, I, F, I, P, P, P, P, SZ, P]
     L.sparse_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     L.sparse_attn_workspace_bytes.restype = SZ
     L.sparse_attn_status_string.argtypes = [I]
@@ -70,7 +76,7 @@ def load():
     L.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
               "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode",
-              "sparse_attn_csa_decode"):
+              "sparse_attn_csa_decode", "sparse_attn_prefill_select", "sparse_attn_prefill"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -254,6 +260,78 @@ def sparse_attn_decode(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_
           _ptr(q_rope), _DTYPE[dt], _ptr(c_kv), _ptr(k_rope), _DTYPE[dt], cs, rs, H, dc, dR,
           float(sm_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), nb, _stream(stream))
     return out, lse, idx_out
+
+
+def sparse_attn_prefill_select(q_idx, w, k_idx, topk, k_scale=None, q_pos=None, kv_len=None,
+                               idx=None, count=None, stream=None):
+    """Fused indexer + Top-K, no score tensor -> (idx [B,T,k] int32 ascending,
+    -1 padded; count [B,T] int32)."""
+    B, T, HI, dI = q_idx.shape
+    L = k_idx.shape[1]
+    _need(q_idx, "q_idx", (torch.bfloat16,))
+    _need(w, "w", (torch.float32,), (B, T, HI))
+    _need(k_idx, "k_idx", (torch.bfloat16, torch.float8_e4m3fn), (B, L, dI))
+    _need(k_scale, "k_scale", (torch.float32,), (B, L), optional=True)
+    _need(q_pos, "q_pos", (torch.int32,), (B, T), optional=True)
+    _need(kv_len, "kv_len", (torch.int32,), (B,), optional=True)
+    dev = q_idx.device
+    if idx is None:
+        idx = torch.empty((B, T, topk), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((B, T), dtype=torch.int32, device=dev)
+    _need(idx, "idx", (torch.int32,), (B, T, topk))
+    _need(count, "count", (torch.int32,), (B, T))
+    _call("sparse_attn_prefill_select", _ptr(q_idx), _DTYPE[q_idx.dtype], _ptr(w), _ptr(k_idx),
+          _DTYPE[k_idx.dtype], _ptr(k_scale), _ptr(q_pos), _ptr(kv_len), B, T, L, HI, dI, topk,
+          _ptr(idx), _ptr(count), _stream(stream))
+    return idx, count
+
+
+def sparse_attn_prefill(q_idx, w, k_idx, topk, q_lat, q_rope, c_kv, k_rope, sm_scale,
+                        k_scale=None, q_pos=None, kv_len=None, mode=SA_PREFILL_SPARSE, out=None,
+                        lse=None, idx_out=None, ws=None, stream=None):
+    """Whole causal prefill -> (out [B,T,H,dc] fp32, lse [B,T,H] fp32).
+
+    mode SA_PREFILL_SPARSE: fused select + sparse MLA (idx_out, if given,
+    receives the sets); SA_PREFILL_DENSE: MLA over every causal candidate
+    (q_idx, w, k_idx may be None); SA_PREFILL_AUTO: dense when L <= topk (the
+    two modes then attend to the same rows).  c_kv / k_rope as in
+    sparse_attn_mla_forward."""
+    B, T, H, dc = q_lat.shape
+    L = c_kv.shape[1]
+    dR = q_rope.shape[-1]
+    _need(q_lat, "q_lat", (torch.bfloat16,))
+    _need(q_rope, "q_rope", (torch.bfloat16,), (B, T, H, dR))
+    _need(c_kv, "c_kv", (torch.bfloat16,), contiguous=False)
+    _need(k_rope, "k_rope", (torch.bfloat16,), contiguous=False)
+    cs, rs = _rows(c_kv, "c_kv", B, L), _rows(k_rope, "k_rope", B, L)
+    dense = mode == SA_PREFILL_DENSE or (mode == SA_PREFILL_AUTO and L <= topk)
+    HI = dI = 0
+    if q_idx is not None:
+        _, _, HI, dI = q_idx.shape
+        _need(q_idx, "q_idx", (torch.bfloat16,), (B, T, HI, dI))
+        _need(w, "w", (torch.float32,), (B, T, HI))
+        _need(k_idx, "k_idx", (torch.bfloat16, torch.float8_e4m3fn), (B, L, dI))
+        _need(k_scale, "k_scale", (torch.float32,), (B, L), optional=True)
+    elif not dense:
+        raise ValueError("the sparse mode needs q_idx, w and k_idx")
+    _need(q_pos, "q_pos", (torch.int32,), (B, T), optional=True)
+    _need(kv_len, "kv_len", (torch.int32,), (B,), optional=True)
+    dev = q_lat.device
+    if out is None:
+        out = torch.empty((B, T, H, dc), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), (B, T, H, dc))
+    _need(lse, "lse", (torch.float32,), (B, T, H))
+    _need(idx_out, "idx_out", (torch.int32,), (B, T, topk), optional=True)
+    ws, nb = _workspace(ws, sparse_attn_workspace_bytes(SA_OP_PREFILL, B, T, L, topk, H, dc), dev)
+    kd = _DTYPE[k_idx.dtype] if k_idx is not None else SA_BF16
+    _call("sparse_attn_prefill", _ptr(q_idx), SA_BF16, _ptr(w), _ptr(k_idx), kd, _ptr(k_scale),
+          _ptr(q_pos), _ptr(kv_len), B, T, L, HI, dI, topk, _ptr(q_lat), _ptr(q_rope), _ptr(c_kv),
+          _ptr(k_rope), cs, rs, H, dc, dR, float(sm_scale), int(mode), _ptr(out), _ptr(lse),
+          _ptr(idx_out), _ptr(ws), nb, _stream(stream))
+    return out, lse
 
 
 def sparse_attn_csa_decode(q_idx, w, k_idx, k_scale, n_comp, topk, q, comp, win, sm_scale,

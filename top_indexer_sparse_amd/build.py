@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "mla.hip", "block_sparse.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "mla.hip", "block_sparse.hip",
+           "prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

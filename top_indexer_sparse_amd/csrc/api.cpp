@@ -90,7 +90,7 @@ int check_mla(const sa::MlaArgs& a, size_t ws_bytes) {
               aligned16(a.idx) && aligned16(a.out) && aligned16(a.lse) && aligned16(a.ws) &&
               (a.c_stride * es) % 16 == 0 && (a.dR == 0 || (a.r_stride * es) % 16 == 0),
           SA_ERR_ALIGN, "mla: pointers and row strides must keep 16-byte alignment");
-  const size_t need = sa::mla_workspace_bytes(a.dtype, a.B, a.T, a.k, a.H, a.dc);
+  const size_t need = sa::mla_workspace_bytes(a.dtype, a.B, a.T, a.k, a.H, a.dc, a.dense != 0);
   REQUIRE(need == 0 || (a.ws && ws_bytes >= need), SA_ERR_WORKSPACE,
           "mla: workspace of %zu bytes required, %zu given", need, a.ws ? ws_bytes : (size_t)0);
   return SA_OK;
@@ -118,6 +118,38 @@ DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype, int n_win =
   off = align256(off + sa::mla_workspace_bytes(kv_dtype, B, 1, k + n_win, H, dc));
   w.total = off;
   return w;
+}
+
+// prefill workspace layout: idx [B, T, k] | count [B, T] | mla ws (the larger
+// of the sparse and the dense attention's)
+struct PrefillWs {
+  size_t idx, count, mla, total;
+};
+PrefillWs prefill_ws(int B, int T, int L, int k, int H, int dc) {
+  PrefillWs w{};
+  size_t off = 0;
+  w.idx = off;
+  off = align256(off + (size_t)B * T * k * sizeof(int32_t));
+  w.count = off;
+  off = align256(off + (size_t)B * T * sizeof(int32_t));
+  w.mla = off;
+  const size_t ms = sa::mla_workspace_bytes(SA_BF16, B, T, k, H, dc);
+  const size_t md = sa::mla_workspace_bytes(SA_BF16, B, T, L < 1 ? 1 : L, H, dc, true);
+  off = align256(off + (ms > md ? ms : md));
+  w.total = off;
+  return w;
+}
+
+int check_prefill_select(const sa::IndexerArgs& a, int k) {
+  int s = check_indexer(a);
+  if (s != SA_OK) return s;
+  REQUIRE(k >= 1, SA_ERR_SHAPE, "prefill_select: k=%d must be >= 1", k);
+  REQUIRE(a.L >= 1, SA_ERR_SHAPE, "prefill_select: L=%d must be >= 1", a.L);
+  REQUIRE(sa::prefill_select_supported(a, k), SA_ERR_UNSUPPORTED,
+          "prefill_select: (q_dtype=%d, k_dtype=%d, HI=%d, dI=%d, L=%d) outside the compiled set "
+          "(bf16 queries, bf16/fp8 keys, HI in {16,32,64,128}, dI in {64,128}, L <= %d)",
+          a.q_dtype, a.k_dtype, a.HI, a.dI, a.L, sa::kPrefillSelectMaxL);
+  return SA_OK;
 }
 
 }  // namespace
@@ -188,6 +220,70 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w, const
   s = hip_status(sa::launch_indexer(ia, st), "decode indexer launch");
   if (s == SA_OK) s = hip_status(sa::launch_topk(ta, st), "decode topk launch");
   if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "decode mla launch");
+  return s;
+}
+
+int sparse_attn_prefill_select(const void* q_idx, int q_dtype, const float* w, const void* k_idx,
+                               int k_dtype, const float* k_scale, const int32_t* q_pos,
+                               const int32_t* kv_len, int B, int T, int L, int HI, int dI, int k,
+                               int32_t* idx, int32_t* count, void* stream) {
+  clear_error();
+  // the score buffer is not used: any non-null pointer passes the indexer checks
+  sa::IndexerArgs a{q_idx, q_dtype, w, k_idx, k_dtype, k_scale, q_pos, kv_len, B, T, L, HI, dI,
+                    (float*)idx};
+  REQUIRE(idx, SA_ERR_NULL, "prefill_select: idx is required");
+  int s = check_prefill_select(a, k);
+  if (s != SA_OK) return s;
+  REQUIRE(aligned16(count), SA_ERR_ALIGN, "prefill_select: count must be 16-byte aligned");
+  return hip_status(sa::launch_prefill_select(a, k, idx, count, (hipStream_t)stream),
+                    "prefill_select launch");
+}
+
+int sparse_attn_prefill(const void* q_idx, int q_idx_dtype, const float* w, const void* k_idx,
+                        int k_dtype, const float* k_scale, const int32_t* q_pos,
+                        const int32_t* kv_len, int B, int T, int L, int HI, int dI, int k,
+                        const void* q_lat, const void* q_rope, const void* c_kv,
+                        const void* k_rope, int64_t c_stride, int64_t r_stride, int H, int dc,
+                        int dR, float sm_scale, int mode, float* out, float* lse,
+                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  REQUIRE(mode == SA_PREFILL_SPARSE || mode == SA_PREFILL_DENSE || mode == SA_PREFILL_AUTO,
+          SA_ERR_SHAPE, "prefill: mode %d not in {SPARSE, DENSE, AUTO}", mode);
+  REQUIRE(B >= 0 && T >= 0 && L >= 1 && k >= 1, SA_ERR_SHAPE,
+          "prefill: bad size B=%d T=%d L=%d k=%d", B, T, L, k);
+  const bool dense = mode == SA_PREFILL_DENSE || (mode == SA_PREFILL_AUTO && L <= k);
+  if (!ws) return fail(SA_ERR_WORKSPACE, "prefill: a workspace is required");
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "prefill: workspace must be 16-byte aligned");
+  const PrefillWs lay = prefill_ws(B, T, L, k, H, dc);
+  char* base = (char*)ws;
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + lay.idx);
+  int32_t* count = (int32_t*)(base + lay.count);
+  sa::IndexerArgs ia{q_idx, q_idx_dtype, w, k_idx, k_dtype, k_scale, q_pos, kv_len, B, T, L, HI, dI,
+                     (float*)idx};
+  sa::MlaArgs ma{q_lat, q_rope, SA_BF16, c_kv, k_rope, c_stride, r_stride, idx, k, B, T, L, H, dc, dR,
+                 sm_scale, out, lse, base + lay.mla};
+  if (dense) {
+    ma.idx = idx;  // unused by the dense attention
+    ma.k = L;
+    ma.dense = 1;
+    ma.dense_q_pos = q_pos;
+    ma.dense_kv_len = kv_len;
+  }
+  int s = dense ? SA_OK : check_prefill_select(ia, k);
+  if (s == SA_OK) s = check_mla(ma, lay.total - lay.mla);
+  if (s == SA_OK && !sa::mla_uses_mfma(ma))
+    s = fail(SA_ERR_UNSUPPORTED, "prefill: the attention needs the bf16 MLA path (dc=512, dR=64, H %% 64 == 0)");
+  if (s == SA_OK && (!aligned16(q_pos) || !aligned16(kv_len) || !aligned16(idx_out)))
+    s = fail(SA_ERR_ALIGN, "prefill: pointers must be 16-byte aligned");
+  if (s == SA_OK && ws_bytes < lay.total)
+    s = fail(SA_ERR_WORKSPACE, "prefill: workspace of %zu bytes required, %zu given", lay.total, ws_bytes);
+  if (s != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (!dense) {
+    s = hip_status(sa::launch_prefill_select(ia, k, idx, count, st), "prefill select launch");
+    ma.count = count;  // the select's lists are ascending and -1 padded
+  }
+  if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "prefill attention launch");
   return s;
 }
 
@@ -282,6 +378,8 @@ size_t sparse_attn_workspace_bytes(int op, int B, int T, int L, int k, int H, in
       return sa::block_workspace_bytes(B, T, L, k, H, dc, 32);
     case SA_OP_CSA_DECODE:  // (B, n_win, Lc, k, H, c) passed as (B, T, L, k, H, dc)
       return decode_ws(B, L, k, H, dc, SA_BF16, T).total;
+    case SA_OP_PREFILL:
+      return prefill_ws(B, T, L, k, H, dc).total;
   }
   return 0;
 }

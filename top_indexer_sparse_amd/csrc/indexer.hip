@@ -19,6 +19,7 @@
 // fp8 keys (OCP e4m3fn) are widened to bf16 in registers (exact) and the
 // per-token scale multiplies the finished score: s*ReLU(x) = ReLU(s*x), s >= 0.
 #include "common.hpp"
+#include "index_core.hpp"
 #include "launch.hpp"
 
 namespace sa {
@@ -107,81 +108,6 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // ---------------------------------------------------------------------------
 // MFMA paths
 // ---------------------------------------------------------------------------
-// Contraction-index map of k-step ks for lane group g (8 consecutive dims):
-//   bf16 keys: dims [32 ks + 8 g, +8)       -> one 16-byte key load per step
-//   fp8 keys : dims [64 (ks/2) + 16 g + 8 (ks%2), +8) -> one 16-byte key load
-//              (16 codes) per two steps
-template <bool FP8>
-__device__ __forceinline__ int kmap(int ks, int g) {
-  return FP8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
-}
-
-// Registers of one 16-position key chunk: KS bf16x8 B operands.
-template <int DI, bool FP8>
-struct KeyChunk {
-  static constexpr int KS = DI / 32;
-  static constexpr int NL = FP8 ? KS / 2 : KS;  // 16-byte loads per lane
-  uintx4 raw[NL];
-  __device__ __forceinline__ void load(const uint8_t* row, int g) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int off = FP8 ? (64 * i + 16 * g) : (2 * (32 * i + 8 * g));
-      raw[i] = *(const uintx4*)(row + off);
-    }
-  }
-  __device__ __forceinline__ bf16x8 operand(int ks) const {
-    if constexpr (!FP8) {
-      return as_bf16x8(raw[ks]);
-    } else {
-      const uintx4& r = raw[ks >> 1];
-      uint32_t c0 = (ks & 1) ? r[2] : r[0];
-      uint32_t c1 = (ks & 1) ? r[3] : r[1];
-      uint32_t o0, o1, o2, o3;
-      fp8x4_to_bf16x4(c0, o0, o1);
-      fp8x4_to_bf16x4(c1, o2, o3);
-      return as_bf16x8(uintx4{o0, o1, o2, o3});
-    }
-  }
-};
-
-// Query operand: qa[ht][ks] = q[h = 16 ht + l%16][kmap(ks, l/16) .. +8]
-template <int HT, int DI, bool FP8>
-struct QueryRegs {
-  static constexpr int KS = DI / 32;
-  bf16x8 a[HT][KS];
-  float wr[HT][4];
-  __device__ __forceinline__ void load(const uint16_t* qrow, const float* wrow,
-                                       int lane) {
-    const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        a[ht][ks] = as_bf16x8(
-            *(const uintx4*)(qrow + (int64_t)(16 * ht + n) * DI + kmap<FP8>(ks, g)));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wr[ht][r] = wrow[16 * ht + 4 * g + r];
-    }
-  }
-  // Score of position (s0 + l%16), summed over all heads, valid in every lane.
-  template <typename Chunk>
-  __device__ __forceinline__ float score(const Chunk& kc) const {
-    bf16x8 kb[KS];  // widened once, shared by every head tile
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = kc.operand(ks);
-    float part = 0.f;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ht][ks], kb[ks], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wr[ht][r], fmaxf(acc[r], 0.f), part);
-    }
-    return sum_over_lane_groups_vx(part);  // callers run it with the whole wave
-  }
-};
-
 // One query per grid row; waves split the positions of the work-group.  Each
 // wave streams a contiguous range through a register ring of R key chunks
 // (16 positions each), so R - 1 chunks (28 KB of bf16 keys per wave at R = 8)

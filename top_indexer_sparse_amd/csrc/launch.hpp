@@ -24,6 +24,12 @@ struct IndexerArgs {
 bool indexer_uses_mfma(const IndexerArgs& a);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
 
+// Fused prefill select (indexer scores + Top-K, the row held in LDS).
+constexpr int kPrefillSelectMaxL = 32768;
+bool prefill_select_supported(const IndexerArgs& a, int topk);
+hipError_t launch_prefill_select(const IndexerArgs& a, int topk, int32_t* idx, int32_t* count,
+                                 hipStream_t st);
+
 struct TopkArgs {
   const float* scores;
   const int32_t* q_pos;
@@ -58,10 +64,19 @@ struct MlaArgs {
   int64_t win_stride = 0;  // elements
   int n_win = 0;
   int zero_rope = 0;
+  // Optional (bf16 MFMA path): dense = 1 attends to every candidate position
+  // s < min(q_pos[bt] + 1, kv_len[b], L) with no index list (idx unused; k
+  // must equal L).
+  const int32_t* dense_q_pos = nullptr;
+  const int32_t* dense_kv_len = nullptr;
+  int dense = 0;
+  // Optional (bf16 MFMA path): count[bt] bounds the index slots that can hold
+  // a position (idx ascending and -1 padded after them).
+  const int32_t* count = nullptr;
 };
 bool mla_uses_mfma(const MlaArgs& a);
 bool mla_supported(const MlaArgs& a);
-size_t mla_workspace_bytes(int dtype, int B, int T, int k, int H, int dc);
+size_t mla_workspace_bytes(int dtype, int B, int T, int k, int H, int dc, bool dense = false);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t st);
 
 struct BlockArgs {

@@ -93,6 +93,14 @@ struct MlaKernelArgs {
   int64_t win_stride_b;
   int n_win;               // slots k .. k+n_win-1 read win rows 0 .. n_win-1
   int zero_rope;           // no RoPE part: q_rope and k_rope read as zeros
+  // DENSE kernels: no index list; slot j of query (b, t) is position j for
+  // every candidate j < min(q_pos[bt] + 1, kv_len[b], L) (either bound may be
+  // null), and a split's slice is not bounded by the slot buffer.
+  const int32_t* q_pos;
+  const int32_t* kv_len;
+  // optional [BT]: only the first count[bt] index slots can hold a position
+  // (an ascending, -1 padded list), so later tiles are not fetched
+  const int32_t* count;
 };
 
 // 128 zero bytes: the RoPE operand of rows that have none.
@@ -103,7 +111,8 @@ __device__ __attribute__((aligned(256))) uint8_t g_mla_zero[128];
 // pair compute the same scores and softmax and split the value product, which
 // halves the accumulators and lets two waves share a SIMD.
 // PACKED: k_rope row = c_kv row + 1024 bytes with one stride ([B, L, 576]).
-template <int NW, bool PACKED, int DS>
+// DENSE: every candidate position, in order, instead of an index list.
+template <int NW, bool PACKED, int DS, bool DENSE>
 __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[kMlaBuf][kMlaTileB];
   __shared__ int spos[kMlaMaxSplitSlots];                  // row to fetch (always valid)
@@ -121,7 +130,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
   const int hg = lin % hgroups;
   const int split = (lin / hgroups) % a.nsplit;
-  const int64_t bt = lin / (hgroups * a.nsplit);
+  int64_t bt = lin / (hgroups * a.nsplit);
+  // dense rows grow with the query position: the longest rows go first
+  if constexpr (DENSE) bt = nblk / (hgroups * a.nsplit) - 1 - bt;
   const int b = (int)(bt / a.T);
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -130,10 +141,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   const int h = hg * HW + hb * 16 + n;       // this lane's head
 
   const int j_begin = split * a.slots_per_split;
-  const int kt = a.k + a.n_win;  // index slots, then window slots
+  // index slots, then window slots; dense: the query's candidate positions
+  int kt = DENSE ? candidate_limit(a.q_pos, a.kv_len, b, bt, a.L) : a.k + a.n_win;
+  if (!DENSE && a.count) kt = min(kt, max(0, a.count[bt]));
   const int nslots = max(0, min(kt, j_begin + a.slots_per_split) - j_begin);
   const uint32_t nrows = (uint32_t)(a.L + a.n_win);  // valid slot values
-  const int32_t* idxr = a.idx + bt * a.k + j_begin;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tiles[0][0];
   const uint32_t lds_spos = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&spos[0];
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   // and 3, laid out per (head block, k-step) as 1 KB runs in the MFMA B
   // operand order, so that the register loads below are conflict-free.
   const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave index in an SGPR
-  {
+  if constexpr (!DENSE) {
     const uint8_t* ib = uniform_ptr((const uint8_t*)(a.idx + bt * a.k));
     const int nrun = (nslots + 63) / 64;
     for (int r = wu; r < nrun; r += NW) {
@@ -221,7 +233,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     // position read placed after one DMA would wait out a full LDS round trip
     uint32_t srow[NLD];
 #pragma unroll
-    for (int i = I0; i < I1; ++i) srow[i] = *(const uint32_t*)(sp + drow[i]);
+    for (int i = I0; i < I1; ++i) {
+      if constexpr (DENSE) {  // slot j is position j_begin + j; past the slice: row 0
+        const int j = tl * kMlaTile + (int)(drow[i] >> 2);
+        srow[i] = j < nslots ? (uint32_t)(j_begin + j) : 0u;
+      } else {
+        srow[i] = *(const uint32_t*)(sp + drow[i]);
+      }
+    }
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const uint32_t s = srow[i] < nrows ? srow[i] : 0u;  // skipped slot: row 0
@@ -254,7 +273,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   for (int t = 0; t < 2; ++t)
     if (t < ntiles) issue(t);
   // per-tile validity masks (bit r: slot 32 t + r holds a position in [0, L))
-  constexpr int kSlotsPerThread = kMlaMaxSplitSlots / (64 * NW);
+  constexpr int kSlotsPerThread = DENSE ? 0 : kMlaMaxSplitSlots / (64 * NW);
 #pragma unroll
   for (int i = 0; i < kSlotsPerThread; ++i) {
     const int j0 = 64 * NW * i;
@@ -405,7 +424,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
     if (more) issue_part(tl + 2, P0{}, P1{});
     const uint8_t* tb = tiles[tl % kMlaBuf];
     const uint8_t* tp = tiles[(tl + kMlaBuf - 1) % kMlaBuf];
-    const uint32_t vm = svmask[tl] >> (4 * g);
+    uint32_t vm;
+    if constexpr (DENSE) {  // the slice's first nslots slots count
+      const int left = nslots - tl * kMlaTile;
+      vm = (left >= kMlaTile ? 0xffffffffu : (1u << left) - 1u) >> (4 * g);
+    } else {
+      vm = svmask[tl] >> (4 * g);
+    }
 
     // S^T[jt]: rows 16 jt + 4 g + r, head n.  The two row blocks are two
     // independent accumulator chains, interleaved.  K operands run kQkAhead
@@ -698,27 +723,29 @@ bool mla_supported(const MlaArgs& a) {
   // the bf16 path addresses a sequence's rows with 32-bit byte offsets
   if (mla_uses_mfma(a))
     return (int64_t)a.L * a.c_stride * 2 < (1LL << 32) && (int64_t)a.L * a.r_stride * 2 < (1LL << 32) &&
-           (int64_t)a.n_win * a.win_stride * 2 < (1LL << 32) && (a.n_win == 0 || a.zero_rope);
-  if (a.n_win || a.zero_rope) return false;  // window rows and RoPE-free rows: bf16 MFMA path only
+           (int64_t)a.n_win * a.win_stride * 2 < (1LL << 32) && (a.n_win == 0 || a.zero_rope) &&
+           (a.dense == 0 || (a.k == a.L && a.n_win == 0));
+  if (a.n_win || a.zero_rope || a.dense) return false;  // bf16 MFMA path only
   if (a.dc > 512 || a.dR > 64 || a.dR < 0 || a.dc < 1) return false;
   if ((int64_t)a.H * a.dc > 256 * kVecMaxOut) return false;
   return vector_lds_bytes(a.H, a.dc, a.dR) <= 64 * 1024;
 }
 
 // KV-split count for the MFMA path: enough work-groups to cover the CUs.
-static int mla_nsplit(int64_t bt, int H, int k) {
+static int mla_nsplit(int64_t bt, int H, int k, bool dense) {
   const int64_t groups = bt * (H / kMlaHeadsWg);
   const int max_split = (k + 2 * kMlaTile - 1) / (2 * kMlaTile);  // >= 64 rows per split
   int ns = 1;
-  while ((int64_t)ns * kMlaMaxSplitSlots < k) ns *= 2;  // one split's slice fits in LDS
+  // an index slice must fit the slot buffer; dense slices have none
+  while (!dense && (int64_t)ns * kMlaMaxSplitSlots < k) ns *= 2;
   while (groups * ns < 256 && ns * 2 <= max_split) ns *= 2;
   return ns;
 }
 
-size_t mla_workspace_bytes(int dtype, int B, int T, int k, int H, int dc) {
+size_t mla_workspace_bytes(int dtype, int B, int T, int k, int H, int dc, bool dense) {
   if (dtype != SA_BF16 || dc != kMlaDc || H % kMlaHeadsWg) return 0;
   const int64_t bt = (int64_t)B * T;
-  const int ns = mla_nsplit(bt, H, k);
+  const int ns = mla_nsplit(bt, H, k, dense);
   if (ns == 1) return 0;
   return (size_t)bt * H * ns * (kMlaDc + 2) * sizeof(float);
 }
@@ -741,13 +768,17 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
     m.win_stride_b = a.win_stride * 2;
     m.n_win = a.n_win;
     m.zero_rope = a.zero_rope;
-    const int kt = a.k + a.n_win;  // slots: the index set, then the window
+    m.q_pos = a.dense_q_pos;
+    m.kv_len = a.dense_kv_len;
+    m.count = a.count;
+    // slots: the index set, then the window; dense: positions 0 .. L-1 (k = L)
+    const int kt = a.k + a.n_win;
     m.idx = a.idx;
     m.k = a.k;
     m.T = a.T;
     m.L = a.L;
     m.H = a.H;
-    m.nsplit = mla_nsplit(bt, a.H, kt);
+    m.nsplit = mla_nsplit(bt, a.H, kt, a.dense);
     m.slots_per_split = ((kt + m.nsplit - 1) / m.nsplit + kMlaTile - 1) / kMlaTile * kMlaTile;
     m.scale_log2 = scale_log2;
     m.out = a.out;
@@ -757,10 +788,17 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t st) {
       m.part_ml = m.part_o + bt * a.H * m.nsplit * kMlaDc;
     }
     const int64_t nblk = bt * (a.H / kMlaHeadsWg) * m.nsplit;
-    if (m.packed)
-      mla_mfma_kernel<kMlaWaves, true, kMlaDs><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
-    else
-      mla_mfma_kernel<kMlaWaves, false, kMlaDs><<<(unsigned)nblk, 64 * kMlaWaves, 0, st>>>(m);
+    const dim3 grid((unsigned)nblk), block(64 * kMlaWaves);
+    if (a.dense) {
+      if (m.packed)
+        mla_mfma_kernel<kMlaWaves, true, kMlaDs, true><<<grid, block, 0, st>>>(m);
+      else
+        mla_mfma_kernel<kMlaWaves, false, kMlaDs, true><<<grid, block, 0, st>>>(m);
+    } else if (m.packed) {
+      mla_mfma_kernel<kMlaWaves, true, kMlaDs, false><<<grid, block, 0, st>>>(m);
+    } else {
+      mla_mfma_kernel<kMlaWaves, false, kMlaDs, false><<<grid, block, 0, st>>>(m);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || m.nsplit == 1) return e;
     mla_combine_kernel<<<(unsigned)(bt * a.H), 128, 0, st>>>(m.part_o, m.part_ml, m.nsplit,

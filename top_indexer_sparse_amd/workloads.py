@@ -329,3 +329,46 @@ def csa_decode(B: int = 32, Lc: int = 32768, HI: int = 64, dI: int = 128,
         nc = torch.as_tensor(n_comp, dtype=torch.int32).reshape(B).contiguous()
     return CsaWorkload("csa_decode", B, Lc, HI, dI, topk, H, c, n_win,
                        1.0 / math.sqrt(c), q_idx, w, k_idx, q, comp, win, nc)
+
+
+W_PREFILL_BATCH = 7
+
+
+def prefill_batch(B: int = 2, T: int = 3000, L: int = 3000, HI: int = 64, dI: int = 128,
+                  topk: int = 256, H: int = 64, dc: int = 512, dR: int = 64,
+                  fp8: bool = False, q_pos: str = "causal", kv_len=None,
+                  with_mla: bool = True, wid: int = W_PREFILL_BATCH) -> DsaWorkload:
+    """Batched prefill with ragged candidate ranges, for the fused prefill select
+    and the prefill modes.  q_pos "causal": query t sits at position t + L - T
+    (the last T positions of the context); "spread": sorted random positions in
+    [0, L).  kv_len: optional per-sequence cache lengths.  fp8: e4m3fn index
+    keys with a per-token scale max|k|/448 (as decode_128k_fp8).  N(0,1)
+    values, w U(0,1)."""
+    q_idx = _randn((B, T, HI, dI), wid, 0).to(torch.bfloat16)
+    w = _rand((B, T, HI), wid, 1)
+    k32 = _randn((B, L, dI), wid, 2)
+    scale = None
+    if fp8:
+        scale = k32.abs().amax(dim=-1) / FP8_MAX
+        scale = torch.where(scale > 0, scale, torch.ones_like(scale)).contiguous()
+        k_idx = (k32 / scale[..., None]).to(torch.float8_e4m3fn)
+    else:
+        k_idx = k32.to(torch.bfloat16)
+    if q_pos == "causal":
+        qp = (torch.arange(T, dtype=torch.int32) + (L - T)).reshape(1, T).repeat(B, 1)
+    else:
+        g = _g(wid, 6)
+        qp = torch.sort(torch.randint(0, L, (B, T), generator=g, dtype=torch.int64), dim=1).values
+        qp = qp.to(torch.int32)
+    kvl = None if kv_len is None else torch.as_tensor(kv_len, dtype=torch.int32).reshape(B)
+    if with_mla:
+        q_lat = _randn((B, T, H, dc), wid, 3).to(torch.bfloat16)
+        q_rope = _randn((B, T, H, dR), wid, 4).to(torch.bfloat16)
+        kv = _randn((B, L, dc + dR), wid, 5).to(torch.bfloat16)
+    else:
+        q_lat = torch.empty((B, 0, H, dc), dtype=torch.bfloat16)
+        q_rope = torch.empty((B, 0, H, dR), dtype=torch.bfloat16)
+        kv = torch.empty((B, 0, dc + dR), dtype=torch.bfloat16)
+    return DsaWorkload("prefill_batch", B, T, L, HI, dI, topk, H, dc, dR,
+                       1.0 / math.sqrt(dc + dR), q_idx, w, k_idx, scale,
+                       qp.contiguous(), kvl, q_lat, q_rope, kv)
