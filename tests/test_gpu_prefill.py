@@ -80,10 +80,10 @@ def _check_select(wl, fp64_rule=True, strict=True):
 @pytest.mark.parametrize("case", [
     dict(B=2, T=3000, L=3000, HI=64, dI=128, topk=256),
     dict(B=2, T=1200, L=5000, HI=64, dI=128, topk=2048, fp8=True),
-    dict(B=3, T=500, L=9000, HI=16, dI=64, topk=512, q_pos="spread", kv_len=[9000, 6000, 100]),
+    dict(B=3, T=501, L=9000, HI=16, dI=64, topk=512, q_pos="spread", kv_len=[9000, 6000, 100]),
     dict(B=1, T=300, L=20000, HI=128, dI=128, topk=1024),
     dict(B=1, T=64, L=32768, HI=64, dI=128, topk=2048),
-    dict(B=2, T=100, L=100, HI=32, dI=128, topk=300, fp8=True),
+    dict(B=2, T=101, L=101, HI=32, dI=128, topk=300, fp8=True),
     dict(B=2, T=40, L=4000, HI=64, dI=64, topk=1, q_pos="spread"),
 ], ids=["causal3000", "fp8_k2048", "spread_ragged", "hi128_L20000", "maxL", "k_above_all",
         "k1"])

@@ -86,4 +86,34 @@ struct QueryRegs {
   }
 };
 
+// Scores of two queries for the same key chunk, which is widened once.  Per
+// head tile the two queries' products form two independent accumulator
+// chains; each query's arithmetic is score()'s, in the same order, so the
+// results carry the same bits.
+template <int HT, int DI, bool FP8, typename Chunk>
+__device__ __forceinline__ void score_pair(const QueryRegs<HT, DI, FP8>& q0,
+                                           const QueryRegs<HT, DI, FP8>& q1, const Chunk& kc,
+                                           float& s0, float& s1) {
+  constexpr int KS = DI / 32;
+  bf16x8 kb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kb[ks] = kc.operand(ks);
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      a0 = mfma16x16x32(q0.a[ht][ks], kb[ks], a0);
+      a1 = mfma16x16x32(q1.a[ht][ks], kb[ks], a1);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p0 = fmaf(q0.wr[ht][r], fmaxf(a0[r], 0.f), p0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p1 = fmaf(q1.wr[ht][r], fmaxf(a1[r], 0.f), p1);
+  }
+  s0 = sum_over_lane_groups_vx(p0);
+  s1 = sum_over_lane_groups_vx(p1);
+}
+
 }  // namespace sa

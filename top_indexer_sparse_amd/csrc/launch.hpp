@@ -26,6 +26,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
 
 // Fused prefill select (indexer scores + Top-K, the row held in LDS).
 constexpr int kPrefillSelectMaxL = 32768;
+constexpr int kPrefillSelectPairMaxL = 16384;  // two rows per work-group up to here
 bool prefill_select_supported(const IndexerArgs& a, int topk);
 hipError_t launch_prefill_select(const IndexerArgs& a, int topk, int32_t* idx, int32_t* count,
                                  hipStream_t st);

@@ -32,11 +32,11 @@
 
 namespace sa {
 
-constexpr int kPfsThreads = 256;
 constexpr int kPfsBins = 2048;
 constexpr int kPfsBinBits = 11;
 
-// Exclusive scan over the work-group's four waves of one int per thread.
+// Exclusive scan over the work-group's NW waves of one int per thread.
+template <int NW>
 __device__ __forceinline__ int pfs_block_excl(int x, int* red, int& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int incl = wave_scan_incl(x);
@@ -46,7 +46,7 @@ __device__ __forceinline__ int pfs_block_excl(int x, int* red, int& total) {
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < kPfsThreads / 64; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int v = red[i];
     before += i < wave ? v : 0;
     total += v;
@@ -54,68 +54,29 @@ __device__ __forceinline__ int pfs_block_excl(int x, int* red, int& total) {
   return incl - x + before;
 }
 
-template <int HT, int DI, bool FP8>
-__global__ __launch_bounds__(kPfsThreads) void pf_select_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ w,
-    const uint8_t* __restrict__ k, const float* __restrict__ kscale,
-    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kv_len,
-    int T, int L, int topk, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-  constexpr int HI = 16 * HT;
-  constexpr int ROWB = FP8 ? DI : 2 * DI;
-  constexpr int R = 16 * HT * DI >= 16384 ? 4 : 8;  // ring depth (as the decode scores)
-  extern __shared__ uintx4 row_v[];                  // round_up(L, 64) + 64 words
-  uint32_t* row = (uint32_t*)row_v;
-  __shared__ uint32_t hist[kPfsBins];
-  __shared__ float spill[4][16];  // scores of ring chunks past a wave's range
-  __shared__ int red[4], red2[4], red3[4], red4[4];
-  __shared__ uint32_t ured[8];
-  __shared__ int found[2];
+template <int NW>
+struct PfsShared {
+  uint32_t hist[kPfsBins];
+  float spill[NW][16];  // scores of ring chunks past a wave's range
+  int red[NW], red2[NW], red3[NW], red4[NW];
+  uint32_t ured[2 * NW];
+  int found[2];
+};
 
-  const int t = T - 1 - (int)blockIdx.x;  // longest rows first
-  const int b = blockIdx.y;
-  const int64_t bt = (int64_t)b * T + t;
+// Steps 2 and 3 for one row of scores held in LDS, run by the whole
+// work-group (NW waves).  Wave w emits positions [w span, (w+1) span) of the
+// row's candidate range [0, lim).
+template <int NW, bool FP8>
+__device__ void pfs_select_row(uint32_t* row, int lim, int span, const float* scb, int topk,
+                               int32_t* out, int32_t* count_out, PfsShared<NW>& sh) {
+  constexpr int NT = 64 * NW;
+  constexpr int BPT = kPfsBins / NT;  // histogram bins per thread
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int lim = candidate_limit(q_pos, kv_len, b, bt, L);
-  // wave quarters: multiples of 16 positions
-  const int span = ((lim + 3) / 4 + 15) & ~15;
-  const int s_begin = wave * span;
-  const int v_end = min(s_begin + span, lim);
-
-  // ---- 1. scores into the LDS row ----
-  if (s_begin < v_end) {  // wave-uniform
-    const uint8_t* kb = k + (int64_t)b * L * ROWB;
-    const int nch = (v_end - s_begin + 15) / 16;
-    auto row_of = [&](int c) {
-      return kb + (int64_t)min(s_begin + 16 * c + n, v_end - 1) * ROWB;
-    };
-    QueryRegs<HT, DI, FP8> qr;
-    qr.load(q + bt * HI * DI, w + bt * HI, lane);
-    // the query has landed before the ring starts, so that the ring's waits
-    // count only its own loads
-    wait_vmcnt<0>();
-    KeyChunk<DI, FP8> ring[R];
-    float* rowf = (float*)row + s_begin;
-    for (int c0 = -R; c0 < nch; c0 += R) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int c = c0 + i;
-        if (c0 >= 0) {  // uniform; chunks past nch are computed and dropped
-          const float sc = qr.score(ring[i]);
-          float* dst = c < nch ? rowf + 16 * c : spill[wave];
-          dst[n] = sc;  // the four lane groups write the same value
-        }
-        ring[i].load(row_of(c + R), g);
-      }
-    }
-  }
-  __syncthreads();
 
   // ---- 2a. keys in place; candidates, smallest and largest key ----
-  const float* scb = FP8 ? kscale + (int64_t)b * L : nullptr;
   int nv = 0;
   uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int s4 = 4 * tid; s4 < lim; s4 += 4 * kPfsThreads) {
+  for (int s4 = 4 * tid; s4 < lim; s4 += 4 * NT) {
     uintx4 v = *(const uintx4*)&row[s4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -137,19 +98,19 @@ __global__ __launch_bounds__(kPfsThreads) void pf_select_kernel(
     const int wnv = wave_total(nv);
     const uint32_t wmn = wave_min_u32(mn), wmx = wave_max_u32(mx);
     if (lane == 0) {
-      red[wave] = wnv;
-      ured[wave] = wmn;
-      ured[4 + wave] = wmx;
+      sh.red[wave] = wnv;
+      sh.ured[wave] = wmn;
+      sh.ured[NW + wave] = wmx;
     }
   }
   __syncthreads();
   int nv_all = 0;
   uint32_t mn_all = 0xffffffffu, mx_all = 0u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    nv_all += red[i];
-    mn_all = min(mn_all, ured[i]);
-    mx_all = max(mx_all, ured[4 + i]);
+  for (int i = 0; i < NW; ++i) {
+    nv_all += sh.red[i];
+    mn_all = min(mn_all, sh.ured[i]);
+    mx_all = max(mx_all, sh.ured[NW + i]);
   }
 
   // ---- 2b. tau and take ----
@@ -159,60 +120,62 @@ __global__ __launch_bounds__(kPfsThreads) void pf_select_kernel(
     uint32_t lo = mn_all;
     const uint32_t range = mx_all - mn_all;
     const int bits = range ? 32 - __builtin_clz(range) : 0;
-    int sh = max(0, bits - kPfsBinBits);
-    uint32_t nb = kPfsBins;  // bins of this pass: the range is [lo, lo + (nb << sh))
+    int sh_bits = max(0, bits - kPfsBinBits);
+    uint32_t nb = kPfsBins;  // bins of this pass: the range is [lo, lo + (nb << sh_bits))
     int r = topk;            // wanted rank, counted from the top inside the range
     for (;;) {
-      for (int i = tid; i < kPfsBins; i += kPfsThreads) hist[i] = 0u;
+      for (int i = tid; i < kPfsBins; i += NT) sh.hist[i] = 0u;
       __syncthreads();
-      for (int s4 = 4 * tid; s4 < lim; s4 += 4 * kPfsThreads) {
+      for (int s4 = 4 * tid; s4 < lim; s4 += 4 * NT) {
         const uintx4 v = *(const uintx4*)&row[s4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = v[e];
           if (s4 + e < lim && key >= lo) {
-            const uint32_t d = (key - lo) >> sh;
-            if (d < nb) atomicAdd(&hist[d], 1u);
+            const uint32_t d = (key - lo) >> sh_bits;
+            if (d < nb) atomicAdd(&sh.hist[d], 1u);
           }
         }
       }
       __syncthreads();
-      // thread i owns bins 2047 - 8 i down to 2040 - 8 i (top first)
-      const int top = kPfsBins - 1 - 8 * tid;
+      // thread i owns bins 2047 - BPT i down to 2048 - BPT (i + 1) (top first)
+      const int top = kPfsBins - 1 - BPT * tid;
       int c = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c += (int)hist[top - j];
+      for (int j = 0; j < BPT; ++j) c += (int)sh.hist[top - j];
       int total;
-      int acc = pfs_block_excl(c, red2, total);  // keys in higher bins
+      int acc = pfs_block_excl<NW>(c, sh.red2, total);  // keys in higher bins
       if (acc < r && r <= acc + c) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int hb = (int)hist[top - j];
+        for (int j = 0; j < BPT; ++j) {
+          const int hb = (int)sh.hist[top - j];
           if (acc < r && r <= acc + hb) {
-            found[0] = top - j;
-            found[1] = acc;
+            sh.found[0] = top - j;
+            sh.found[1] = acc;
           }
           acc += hb;
         }
       }
       __syncthreads();
-      const int bin = found[0], above = found[1];
+      const int bin = sh.found[0], above = sh.found[1];
       r -= above;
-      lo += (uint32_t)bin << sh;
-      if (sh == 0) {
+      lo += (uint32_t)bin << sh_bits;
+      if (sh_bits == 0) {
         tau = lo;
         take = r;
         break;
       }
-      // the next pass splits this bin, 2^sh keys wide, into at most 2048 bins
-      const int sh_next = max(0, sh - kPfsBinBits);
-      nb = 1u << (sh - sh_next);
-      sh = sh_next;
+      // the next pass splits this bin, 2^sh_bits keys wide, into at most 2048 bins
+      const int sh_next = max(0, sh_bits - kPfsBinBits);
+      nb = 1u << (sh_bits - sh_next);
+      sh_bits = sh_next;
     }
   }
   const int cnt = min(nv_all, topk);
 
   // ---- 3. emit in position order ----
+  const int s_begin = wave * span;
+  const int v_end = min(s_begin + span, lim);
   int gt = 0, eq = 0;
   for (int s4 = s_begin + 4 * lane; s4 < v_end; s4 += 256) {
     const uintx4 v = *(const uintx4*)&row[s4];
@@ -226,18 +189,17 @@ __global__ __launch_bounds__(kPfsThreads) void pf_select_kernel(
   {
     const int wgt = wave_total(gt), weq = wave_total(eq);
     if (lane == 0) {
-      red3[wave] = wgt;
-      red4[wave] = weq;
+      sh.red3[wave] = wgt;
+      sh.red4[wave] = weq;
     }
   }
   __syncthreads();
   int base = 0, eq_before = 0;
   for (int i = 0; i < wave; ++i) {
-    const int ti = min(max(take - eq_before, 0), red4[i]);  // ties wave i takes
-    base += red3[i] + ti;
-    eq_before += red4[i];
+    const int ti = min(max(take - eq_before, 0), sh.red4[i]);  // ties wave i takes
+    base += sh.red3[i] + ti;
+    eq_before += sh.red4[i];
   }
-  int32_t* out = idx + bt * topk;
   int run_sel = 0, run_eq = 0;
   for (int s0 = s_begin; s0 < v_end; s0 += 256) {  // uniform rounds of 64 x 4
     const int s4 = s0 + 4 * lane;
@@ -273,14 +235,103 @@ __global__ __launch_bounds__(kPfsThreads) void pf_select_kernel(
     run_sel += __builtin_amdgcn_readlane(sel_incl, 63);
     run_eq += __builtin_amdgcn_readlane(eq_incl, 63);
   }
-  for (int j = cnt + tid; j < topk; j += kPfsThreads) out[j] = -1;
-  if (tid == 0 && count) count[bt] = cnt;
+  for (int j = cnt + tid; j < topk; j += NT) out[j] = -1;
+  if (tid == 0 && count_out) *count_out = cnt;
+}
+
+// QPW query rows per work-group of 4 QPW waves.  With QPW = 2 (two adjacent
+// queries) every key chunk a wave loads feeds both queries' products, which
+// halves the key traffic into the CU; the two rows then take 2 x 4 bytes per
+// position of LDS, so QPW = 2 serves L <= 16384 and HI <= 64.
+template <int HT, int DI, bool FP8, int QPW>
+__global__ __launch_bounds__(256 * QPW) void pf_select_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ k, const float* __restrict__ kscale,
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kv_len,
+    int T, int L, int rowwords, int topk, int32_t* __restrict__ idx,
+    int32_t* __restrict__ count) {
+  constexpr int NW = 4 * QPW;
+  constexpr int HI = 16 * HT;
+  constexpr int ROWB = FP8 ? DI : 2 * DI;
+  // ring depth: as the decode scores for one query; two queries' operands
+  // leave room for four chunks
+  constexpr int R = QPW == 2 ? 4 : (16 * HT * DI >= 16384 ? 4 : 8);
+  extern __shared__ uintx4 row_v[];  // QPW rows of rowwords words
+  uint32_t* rows = (uint32_t*)row_v;
+  __shared__ PfsShared<NW> sh;
+
+  const int npair = (T + QPW - 1) / QPW;
+  const int t0 = QPW * (npair - 1 - (int)blockIdx.x);  // longest rows first
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  int lim[QPW];
+  int64_t bt[QPW];
+  int lim_max = 0;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int t = min(t0 + i, T - 1);  // a missing second query repeats the first
+    bt[i] = (int64_t)b * T + t;
+    lim[i] = candidate_limit(q_pos, kv_len, b, bt[i], L);
+    lim_max = max(lim_max, lim[i]);
+  }
+  // wave parts: multiples of 16 positions
+  const int span = ((lim_max + NW - 1) / NW + 15) & ~15;
+  const int s_begin = wave * span;
+  const int v_end = min(s_begin + span, lim_max);
+
+  // ---- 1. scores into the LDS rows ----
+  if (s_begin < v_end) {  // wave-uniform
+    const uint8_t* kb = k + (int64_t)b * L * ROWB;
+    const int nch = (v_end - s_begin + 15) / 16;
+    auto row_of = [&](int c) {
+      return kb + (int64_t)min(s_begin + 16 * c + n, v_end - 1) * ROWB;
+    };
+    QueryRegs<HT, DI, FP8> qr[QPW];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) qr[i].load(q + bt[i] * HI * DI, w + bt[i] * HI, lane);
+    // the queries have landed before the ring starts, so that the ring's
+    // waits count only its own loads
+    wait_vmcnt<0>();
+    KeyChunk<DI, FP8> ring[R];
+    for (int c0 = -R; c0 < nch; c0 += R) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int c = c0 + i;
+        if (c0 >= 0) {  // uniform; chunks past nch are computed and dropped
+          float sc[QPW];
+          if constexpr (QPW == 2)
+            score_pair(qr[0], qr[1], ring[i], sc[0], sc[1]);
+          else
+            sc[0] = qr[0].score(ring[i]);
+#pragma unroll
+          for (int qi = 0; qi < QPW; ++qi) {
+            float* dst = c < nch ? (float*)rows + qi * rowwords + s_begin + 16 * c
+                                 : sh.spill[wave];
+            dst[n] = sc[qi];  // the four lane groups write the same value
+          }
+        }
+        ring[i].load(row_of(c + R), g);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2, 3. one row after the other, by the whole work-group ----
+  const float* scb = FP8 ? kscale + (int64_t)b * L : nullptr;
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) {
+    if (t0 + qi >= T) break;  // uniform
+    if (qi > 0) __syncthreads();
+    pfs_select_row<NW, FP8>(rows + qi * rowwords, lim[qi], span, scb, topk,
+                            idx + bt[qi] * topk, count ? count + bt[qi] : nullptr, sh);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-size_t prefill_select_lds_bytes(int L) { return ((size_t)((L + 63) / 64) * 64 + 64) * 4; }
+static int pfs_rowwords(int L) { return (L + 63) / 64 * 64 + 64; }
 
 bool prefill_select_supported(const IndexerArgs& a, int topk) {
   if (!indexer_uses_mfma(a)) return false;
@@ -289,33 +340,45 @@ bool prefill_select_supported(const IndexerArgs& a, int topk) {
   return true;
 }
 
-template <int HT, int DI, bool FP8>
+template <int HT, int DI, bool FP8, int QPW>
 static hipError_t launch_pfs(const IndexerArgs& a, int topk, int32_t* idx, int32_t* count,
                              hipStream_t st) {
-  const size_t lds = prefill_select_lds_bytes(a.L);
+  const int rowwords = pfs_rowwords(a.L);
+  const size_t lds = (size_t)QPW * rowwords * 4;
   static bool attr_set = false;  // the opt-in is per kernel and process-wide
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)pf_select_kernel<HT, DI, FP8>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)prefill_select_lds_bytes(kPrefillSelectMaxL));
+    const int most = QPW * pfs_rowwords(QPW == 2 ? kPrefillSelectPairMaxL : kPrefillSelectMaxL) * 4;
+    hipError_t e = hipFuncSetAttribute((const void*)pf_select_kernel<HT, DI, FP8, QPW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((unsigned)a.T, (unsigned)a.B);
-  pf_select_kernel<HT, DI, FP8><<<grid, kPfsThreads, lds, st>>>(
-      (const uint16_t*)a.q, a.w, (const uint8_t*)a.k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, topk,
-      idx, count);
+  dim3 grid((unsigned)((a.T + QPW - 1) / QPW), (unsigned)a.B);
+  pf_select_kernel<HT, DI, FP8, QPW><<<grid, 256 * QPW, lds, st>>>(
+      (const uint16_t*)a.q, a.w, (const uint8_t*)a.k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L,
+      rowwords, topk, idx, count);
   return hipGetLastError();
+}
+
+// two queries per work-group where both rows fit and the two query blocks fit
+// the registers (HI <= 64); one otherwise
+template <int HT, int DI, bool FP8>
+static hipError_t launch_pfs_q(const IndexerArgs& a, int topk, int32_t* idx, int32_t* count,
+                               hipStream_t st) {
+  if constexpr (HT <= 4)
+    if (a.L <= kPrefillSelectPairMaxL && a.T >= 2)
+      return launch_pfs<HT, DI, FP8, 2>(a, topk, idx, count, st);
+  return launch_pfs<HT, DI, FP8, 1>(a, topk, idx, count, st);
 }
 
 template <int DI, bool FP8>
 static hipError_t pfs_dispatch_ht(const IndexerArgs& a, int topk, int32_t* idx, int32_t* count,
                                   hipStream_t st) {
   switch (a.HI / 16) {
-    case 1: return launch_pfs<1, DI, FP8>(a, topk, idx, count, st);
-    case 2: return launch_pfs<2, DI, FP8>(a, topk, idx, count, st);
-    case 4: return launch_pfs<4, DI, FP8>(a, topk, idx, count, st);
-    case 8: return launch_pfs<8, DI, FP8>(a, topk, idx, count, st);
+    case 1: return launch_pfs_q<1, DI, FP8>(a, topk, idx, count, st);
+    case 2: return launch_pfs_q<2, DI, FP8>(a, topk, idx, count, st);
+    case 4: return launch_pfs_q<4, DI, FP8>(a, topk, idx, count, st);
+    case 8: return launch_pfs_q<8, DI, FP8>(a, topk, idx, count, st);
   }
   return hipErrorInvalidValue;
 }
