@@ -213,7 +213,10 @@ int sparse_attn_prefill_select(const void* q_idx, int q_dtype, const float* w,
 /* ---------------------------------------------------------------------------
  * Prefill: every query of a causal prefill, in one call.
  *   mode SA_PREFILL_SPARSE: sparse_attn_prefill_select, then stage 3 over the
- *     selected rows ("Sparse Attention 数学学习笔记" §8-§9).
+ *     selected rows ("Sparse Attention 数学学习笔记" §8-§9).  Above the fused
+ *     select's L <= 32768 the sets come from stages 1 and 2 run per sequence
+ *     in chunks of 4096 query rows, through a [4096, L] score buffer in the
+ *     workspace (the same sets).
  *   mode SA_PREFILL_DENSE: stage 3 over every candidate position s <
  *     min(q_pos[b,t] + 1, kv_len[b], L), with no indexer and no Top-K: the
  *     dense attention with a causal mask that "LLM注意力优化：稀疏注意力" (DSA
@@ -229,8 +232,9 @@ int sparse_attn_prefill_select(const void* q_idx, int q_dtype, const float* w,
  * the dense mode) and sparse_attn_mla_forward (q_lat [B,T,H,dc], q_rope
  * [B,T,H,dR], strided c_kv / k_rope rows).  idx_out [B,T,k] (may be NULL;
  * sparse mode only) receives the selected sets.
- * Compiled set: the prefill select's, and the bf16 MLA path ((dc, dR) =
- * (512, 64), H a multiple of 64).
+ * Compiled set: the prefill select's (any L in the sparse mode: longer rows
+ * take the chunked path, whose top-k set is 1 <= k <= 4096), and the bf16
+ * MLA path ((dc, dR) = (512, 64), H a multiple of 64).
  * ws: sparse_attn_workspace_bytes(SA_OP_PREFILL, B, T, L, k, H, dc), which
  * covers every mode.
  * ------------------------------------------------------------------------- */

@@ -263,3 +263,26 @@ def test_prefill_dense_fullsize_sampled():
     ro, rl = oracle.masked_mla(wl.q_lat[:, rows].contiguous(), wl.q_rope[:, rows].contiguous(),
                                wl.kv, vis, wl.sm_scale, dc=wl.dc)
     assert_attention_close(out[:, rows], ro, ATTN_ATOL_BF16, lse[:, rows], rl)
+
+
+def test_prefill_sparse_long_rows_chunked():
+    # rows above the fused select's 32768 positions take the staged select in
+    # chunks of 4096 query rows per sequence: 2 sequences x (4096 + 104) rows
+    _announce("prefill sparse L=33000 T=4200 B=2 (chunked select)")
+    wl = workloads.prefill_batch(B=2, T=4200, L=33000, HI=64, dI=128, topk=2048, H=64)
+    t = wl.to(DEV)
+    idx = torch.empty((wl.B, wl.T, wl.topk), dtype=torch.int32, device=DEV)
+    out, lse = _prefill(t, wl, api.SA_PREFILL_SPARSE, idx_out=idx)
+    s = api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, q_pos=t.q_pos)
+    si, sc = api.sparse_attn_topk(s, wl.topk, q_pos=t.q_pos)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, si.cpu().numpy())
+    rows = [0, 4095, 4096, 4199]
+    sr = s[:, rows].cpu().double().numpy()
+    oi, oc = oracle.topk(sr, wl.topk, q_pos=wl.q_pos[:, rows].contiguous())
+    assert np.array_equal(gi[:, rows], oi)
+    del s
+    ro, rl = oracle.sparse_mla(wl.q_lat[:, rows].contiguous(), wl.q_rope[:, rows].contiguous(),
+                               wl.kv, gi[:, rows], wl.sm_scale, dc=wl.dc)
+    assert_attention_close(out[:, rows], ro, ATTN_ATOL_BF16, lse[:, rows], rl)

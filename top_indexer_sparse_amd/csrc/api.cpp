@@ -120,10 +120,17 @@ DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype, int n_win =
   return w;
 }
 
+// Rows longer than the fused select's on-chip row take the staged select in
+// chunks of this many query rows: a [chunk, L] score buffer instead of
+// [B, T, L], and enough rows per chunk (512 score work-groups) to fill the GPU.
+constexpr int kPrefillChunkRows = 4096;
+
 // prefill workspace layout: idx [B, T, k] | count [B, T] | mla ws (the larger
-// of the sparse and the dense attention's)
+// of the sparse and the dense attention's) | for L above the fused select's
+// limit: chunk scores [chunk, L] | top-k ws of one chunk
 struct PrefillWs {
-  size_t idx, count, mla, total;
+  size_t idx, count, mla, scores, topk, total;
+  int chunk;  // query rows per staged chunk (0: the fused select runs)
 };
 PrefillWs prefill_ws(int B, int T, int L, int k, int H, int dc) {
   PrefillWs w{};
@@ -136,16 +143,28 @@ PrefillWs prefill_ws(int B, int T, int L, int k, int H, int dc) {
   const size_t ms = sa::mla_workspace_bytes(SA_BF16, B, T, k, H, dc);
   const size_t md = sa::mla_workspace_bytes(SA_BF16, B, T, L < 1 ? 1 : L, H, dc, true);
   off = align256(off + (ms > md ? ms : md));
+  w.chunk = 0;
+  w.scores = w.topk = off;
+  if (L > sa::kPrefillSelectMaxL && T > 0) {
+    w.chunk = T < kPrefillChunkRows ? T : kPrefillChunkRows;
+    off = align256(off + (size_t)w.chunk * L * sizeof(float));
+    w.topk = off;
+    off = align256(off + sa::topk_workspace_bytes(1, w.chunk, L, k < 1 ? 1 : k));
+  }
   w.total = off;
   return w;
 }
 
-int check_prefill_select(const sa::IndexerArgs& a, int k) {
+// allow_long: rows above the fused select's limit are accepted (the prefill
+// entry point then selects through chunked score buffers)
+int check_prefill_select(const sa::IndexerArgs& a, int k, bool allow_long = false) {
   int s = check_indexer(a);
   if (s != SA_OK) return s;
   REQUIRE(k >= 1, SA_ERR_SHAPE, "prefill_select: k=%d must be >= 1", k);
   REQUIRE(a.L >= 1, SA_ERR_SHAPE, "prefill_select: L=%d must be >= 1", a.L);
-  REQUIRE(sa::prefill_select_supported(a, k), SA_ERR_UNSUPPORTED,
+  REQUIRE(sa::prefill_select_supported(a, k) ||
+              (allow_long && a.L > sa::kPrefillSelectMaxL && sa::indexer_uses_mfma(a)),
+          SA_ERR_UNSUPPORTED,
           "prefill_select: (q_dtype=%d, k_dtype=%d, HI=%d, dI=%d, L=%d) outside the compiled set "
           "(bf16 queries, bf16/fp8 keys, HI in {16,32,64,128}, dI in {64,128}, L <= %d)",
           a.q_dtype, a.k_dtype, a.HI, a.dI, a.L, sa::kPrefillSelectMaxL);
@@ -269,7 +288,11 @@ int sparse_attn_prefill(const void* q_idx, int q_idx_dtype, const float* w, cons
     ma.dense_q_pos = q_pos;
     ma.dense_kv_len = kv_len;
   }
-  int s = dense ? SA_OK : check_prefill_select(ia, k);
+  int s = dense ? SA_OK : check_prefill_select(ia, k, true);
+  if (s == SA_OK && !dense && lay.chunk > 0) {
+    REQUIRE(sa::topk_supported(L, k), SA_ERR_UNSUPPORTED,
+            "prefill: k=%d, L=%d outside the top-k set", k, L);
+  }
   if (s == SA_OK) s = check_mla(ma, lay.total - lay.mla);
   if (s == SA_OK && !sa::mla_uses_mfma(ma))
     s = fail(SA_ERR_UNSUPPORTED, "prefill: the attention needs the bf16 MLA path (dc=512, dR=64, H %% 64 == 0)");
@@ -279,10 +302,28 @@ int sparse_attn_prefill(const void* q_idx, int q_idx_dtype, const float* w, cons
     s = fail(SA_ERR_WORKSPACE, "prefill: workspace of %zu bytes required, %zu given", lay.total, ws_bytes);
   if (s != SA_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (!dense) {
+  if (!dense && lay.chunk == 0) {
     s = hip_status(sa::launch_prefill_select(ia, k, idx, count, st), "prefill select launch");
-    ma.count = count;  // the select's lists are ascending and -1 padded
+  } else if (!dense) {
+    // staged select per sequence and chunk of query rows (one-sequence views)
+    const size_t qrow = (size_t)HI * dI * 2, krow = (size_t)dI * (k_dtype == SA_FP8_E4M3 ? 1 : 2);
+    float* scores = (float*)(base + lay.scores);
+    for (int b = 0; b < B && s == SA_OK; ++b) {
+      for (int t0 = 0; t0 < T && s == SA_OK; t0 += lay.chunk) {
+        const int tc = T - t0 < lay.chunk ? T - t0 : lay.chunk;
+        const int64_t r0 = (int64_t)b * T + t0;
+        sa::IndexerArgs ci{(const char*)q_idx + r0 * qrow, q_idx_dtype, w + r0 * HI,
+                           (const char*)k_idx + (int64_t)b * L * krow, k_dtype,
+                           k_scale ? k_scale + (int64_t)b * L : nullptr, q_pos ? q_pos + r0 : nullptr,
+                           kv_len ? kv_len + b : nullptr, 1, tc, L, HI, dI, scores};
+        sa::TopkArgs ct{scores, q_pos ? q_pos + r0 : nullptr, kv_len ? kv_len + b : nullptr, 1, tc, L, k,
+                        idx + r0 * k, count + r0, base + lay.topk};
+        s = hip_status(sa::launch_indexer(ci, st), "prefill chunk indexer launch");
+        if (s == SA_OK) s = hip_status(sa::launch_topk(ct, st), "prefill chunk topk launch");
+      }
+    }
   }
+  if (!dense) ma.count = count;  // the select's lists are ascending and -1 padded
   if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "prefill attention launch");
   return s;
 }
