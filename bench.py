@@ -101,7 +101,17 @@ def cpu_baseline(wl, budget_s=20.0):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_32k_traffic.md")
-INDEXER_SRC = os.path.join(ROOT, "top_indexer_sparse_amd", "csrc", "indexer.hip")
+# the decode score kernel's source: its translation unit and the headers it uses
+INDEXER_SRC = [os.path.join(ROOT, "top_indexer_sparse_amd", "csrc", f)
+               for f in ("indexer.hip", "index_core.hpp", "common.hpp")]
+
+
+def indexer_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in INDEXER_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -109,7 +119,6 @@ def measured_traffic():
     summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the
     factor a plain device copy of known size gives.  None when the summary is
     missing or was taken on other indexer source."""
-    import hashlib
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -119,8 +128,7 @@ def measured_traffic():
         if line.startswith("- ") and ":" in line:
             key, _, v = line[2:].partition(":")
             vals[key.strip()] = v.strip().strip("`")
-    sha = hashlib.sha256(open(INDEXER_SRC, "rb").read()).hexdigest()
-    if vals.get("indexer_source_sha256") != sha:
+    if vals.get("indexer_source_sha256") != indexer_source_sha256():
         return None
     try:
         fetch = float(vals["fetch_kib_per_launch"]) * 1024 * float(vals["fetch_scale"])
