@@ -173,6 +173,25 @@ def test_prefill_sparse_mode():
     assert_attention_close(out, ro, ATTN_ATOL_BF16, lse, rl)
 
 
+def test_prefill_sparse_mode_fp8_ragged():
+    _announce("prefill sparse fp8 keys, spread q_pos, ragged kv_len")
+    wl = workloads.prefill_batch(B=2, T=400, L=1500, HI=64, dI=128, topk=256, H=64, fp8=True,
+                                 q_pos="spread", kv_len=[1500, 900])
+    t = wl.to(DEV)
+    idx = torch.empty((wl.B, wl.T, wl.topk), dtype=torch.int32, device=DEV)
+    out, lse = _prefill(t, wl, api.SA_PREFILL_SPARSE, idx_out=idx)
+    s = api.sparse_attn_indexer_scores(t.q_idx, t.w, t.k_idx, k_scale=t.k_scale, q_pos=t.q_pos,
+                                       kv_len=t.kv_len)
+    si, sc = api.sparse_attn_topk(s, wl.topk, q_pos=t.q_pos, kv_len=t.kv_len)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, si.cpu().numpy())
+    oi, oc = oracle.topk(s.cpu().double().numpy(), wl.topk, q_pos=wl.q_pos, kv_len=wl.kv_len)
+    assert np.array_equal(gi, oi)
+    ro, rl = oracle.sparse_mla(wl.q_lat, wl.q_rope, wl.kv, gi, wl.sm_scale, dc=wl.dc)
+    assert_attention_close(out, ro, ATTN_ATOL_BF16, lse, rl)
+
+
 def _visible(wl):
     L = wl.L
     qp = wl.q_pos.numpy().astype(np.int64)
