@@ -345,14 +345,12 @@ static hipError_t launch_pfs(const IndexerArgs& a, int topk, int32_t* idx, int32
                              hipStream_t st) {
   const int rowwords = pfs_rowwords(a.L);
   const size_t lds = (size_t)QPW * rowwords * 4;
-  static bool attr_set = false;  // the opt-in is per kernel and process-wide
-  if (!attr_set) {
-    const int most = QPW * pfs_rowwords(QPW == 2 ? kPrefillSelectPairMaxL : kPrefillSelectMaxL) * 4;
-    hipError_t e = hipFuncSetAttribute((const void*)pf_select_kernel<HT, DI, FP8, QPW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // the opt-in to more than 64 KB of dynamic LDS, set on every launch (a host
+  // call; it keeps no per-device or per-thread state here)
+  const int most = QPW * pfs_rowwords(QPW == 2 ? kPrefillSelectPairMaxL : kPrefillSelectMaxL) * 4;
+  hipError_t e = hipFuncSetAttribute((const void*)pf_select_kernel<HT, DI, FP8, QPW>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, most);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)((a.T + QPW - 1) / QPW), (unsigned)a.B);
   pf_select_kernel<HT, DI, FP8, QPW><<<grid, 256 * QPW, lds, st>>>(
       (const uint16_t*)a.q, a.w, (const uint8_t*)a.k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L,

@@ -494,6 +494,7 @@ constexpr int kSpMaxRows = 128;    // rows of a launch taking the split path
 constexpr int kSpMinL = 8192;      // shortest row length taking it
 constexpr int kSpMaxChunks = 256;  // rows up to 1M positions
 constexpr int kSpKeep = 16384;     // kept keys the second launch holds in LDS
+constexpr int kSpSelThreads = 512; // threads of a select work-group (one per row)
 
 struct TopkSplitArgs {
   const float* scores;
@@ -509,7 +510,8 @@ struct TopkSplitArgs {
   int32_t* count;      // [rows] or null
 };
 
-// Exclusive block scan over the 256 threads of a split work-group.
+// Exclusive block scan over the NT threads of a split work-group.
+template <int NT = kSpThreads>
 __device__ __forceinline__ int sp_scan_excl(int x, int* red, int& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int incl = wave_scan_incl(x);
@@ -519,7 +521,7 @@ __device__ __forceinline__ int sp_scan_excl(int x, int* red, int& total) {
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kSpWaves; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int v = red[w];
     before += w < wave ? v : 0;
     total += v;
@@ -529,40 +531,44 @@ __device__ __forceinline__ int sp_scan_excl(int x, int* red, int& total) {
 
 // Bins of `hist` (2048 bins) holding ranks r0 <= r1 counted from the top:
 // found[0] = bin of r0, found[1] = entries in higher bins, found[2] = bin of
-// r1; a rank outside [1, total] gives bin -1.  Thread t owns bins
-// 2047 - 8t .. 2040 - 8t.  Starts with a barrier (the histogram is
-// complete); `found` is visible when it returns.
+// r1; a rank outside [1, total] gives bin -1.  Thread t owns the BPT =
+// 2048 / NT bins 2047 - BPT t downwards.  Starts with a barrier (the
+// histogram is complete); `found` is visible when it returns.
+template <int NT = kSpThreads>
 __device__ __forceinline__ void sp_rank_bins(const int* hist, int r0, int r1, int* red,
                                              int* found) {
+  constexpr int BPT = kSpBins / NT;
   __syncthreads();
   const int tid = threadIdx.x;
   if (tid == 0) {
     found[0] = found[2] = -1;
     found[1] = 0;
   }
-  int h[8], own = 0;
+  int h[BPT], own = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = hist[kSpBins - 1 - 8 * tid - e];
+  for (int e = 0; e < BPT; ++e) {
+    h[e] = hist[kSpBins - 1 - BPT * tid - e];
     own += h[e];
   }
   int total;
-  int above = sp_scan_excl(own, red, total);
+  int above = sp_scan_excl<NT>(own, red, total);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < BPT; ++e) {
     if (above < r0 && r0 <= above + h[e]) {
-      found[0] = kSpBins - 1 - 8 * tid - e;
+      found[0] = kSpBins - 1 - BPT * tid - e;
       found[1] = above;
     }
-    if (above < r1 && r1 <= above + h[e]) found[2] = kSpBins - 1 - 8 * tid - e;
+    if (above < r1 && r1 <= above + h[e]) found[2] = kSpBins - 1 - BPT * tid - e;
     above += h[e];
   }
   __syncthreads();
 }
+template <int NT = kSpThreads>
 __device__ __forceinline__ void sp_rank_bin(const int* hist, int r, int* red, int* found) {
-  sp_rank_bins(hist, r, r, red, found);
+  sp_rank_bins<NT>(hist, r, r, red, found);
 }
 
+template <int NT = kSpThreads>
 __device__ __forceinline__ int sp_block_sum(int x, int* red) {
   const int t = wave_total(x);
   __syncthreads();
@@ -570,7 +576,7 @@ __device__ __forceinline__ int sp_block_sum(int x, int* red) {
   __syncthreads();
   int total = 0;
 #pragma unroll
-  for (int w = 0; w < kSpWaves; ++w) total += red[w];
+  for (int w = 0; w < NT / 64; ++w) total += red[w];
   return total;
 }
 
@@ -699,12 +705,14 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
   }
 }
 
-// Launch B: one 256-thread work-group per row.
-__global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplitArgs a) {
+// Launch B: one NT-thread work-group per row.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) {
+  constexpr int kSelWaves = NT / 64;
   __shared__ uint32_t kk[kSpKeep];
   __shared__ int32_t kp[kSpKeep];
   __shared__ int hist[kSpBins];
-  __shared__ int red[kSpWaves];
+  __shared__ int red[kSelWaves];
   __shared__ int found[3];
   __shared__ int preK[kSpMaxChunks + 1];
   __shared__ int tot[4];
@@ -729,9 +737,9 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
       cc = c4.z;
     }
     int tK;
-    const int ek = sp_scan_excl(ca + ci, red, tK);
-    const int tA = sp_block_sum(ca, red);
-    const int tC = sp_block_sum(cc, red);
+    const int ek = sp_scan_excl<NT>(ca + ci, red, tK);
+    const int tA = sp_block_sum<NT>(ca, red);
+    const int tC = sp_block_sum<NT>(cc, red);
     if (tid < nch) preK[tid] = ek;
     if (tid == 0) {
       preK[nch] = tK;
@@ -750,7 +758,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
     // ---- kept keys into LDS (chunk order = position order): 256 / nch
     //      threads per chunk, 16 loads in flight per thread and batch ----
     {
-      const int tpc = kSpThreads / nch;  // >= 1
+      const int tpc = NT / nch;  // >= 1
       const int c = tid / tpc, r = tid % tpc;
       if (c < nch) {
         const int n_c = preK[c + 1] - preK[c];
@@ -791,17 +799,17 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
       const int s2 = top + 1 - width;
       const uint32_t dmask = (1u << width) - 1u;
       __syncthreads();  // kept keys stored / previous bins read
-      for (int i = tid; i < kSpBins; i += kSpThreads) hist[i] = 0;
+      for (int i = tid; i < kSpBins; i += NT) hist[i] = 0;
       if (tid == 0) nsmall = 0;
       __syncthreads();
 #pragma unroll 1
-      for (int j0 = 0; j0 < K; j0 += kSpThreads) {
+      for (int j0 = 0; j0 < K; j0 += NT) {
         const int j = j0 + tid;
         const uint32_t key = j < K ? kk[j] : 0u;
         const uint32_t c = key - lo;
         hist_add(hist, (c >> s2) & dmask, j < K && key <= hi && (c & pmask) == prefix);
       }
-      sp_rank_bin(hist, krem, red, found);
+      sp_rank_bin<NT>(hist, krem, red, found);
       prefix |= (uint32_t)found[0] << s2;
       pmask |= dmask << s2;
       krem -= found[1];
@@ -809,7 +817,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
       if (top >= 0 && hist[found[0]] <= 64) {
         // few keys left in the bin: one wave ranks them directly
 #pragma unroll 1
-        for (int j0 = 0; j0 < K; j0 += kSpThreads) {
+        for (int j0 = 0; j0 < K; j0 += NT) {
           const int j = j0 + tid;
           const uint32_t key = j < K ? kk[j] : 0u;
           if (j < K && key <= hi && ((key - lo) & pmask) == prefix) small[atomicAdd(&nsmall, 1)] = key;
@@ -844,12 +852,12 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
     }
     // ---- ascending output: thread t scans its run of the kept keys ----
     __syncthreads();
-    const int s = (K + kSpThreads - 1) / kSpThreads;  // <= 64
+    const int s = (K + NT - 1) / NT;  // <= 64
     const int j0 = tid * s, j1 = min(K, j0 + s);
     int c = 0;
     for (int j = j0; j < j1; ++j) c += ((kk[j] > tau) << 16) | (kk[j] == tau);
     int total;
-    const int before = sp_scan_excl(c, red, total);  // gt, eq <= 16384 each
+    const int before = sp_scan_excl<NT>(c, red, total);  // gt, eq <= 16384 each
     int gtb = before >> 16, eqb = before & 0xffff;
     for (int j = j0; j < j1; ++j) {
       const bool g = kk[j] > tau, eq = kk[j] == tau;
@@ -870,15 +878,15 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
         const int s2 = pass == 0 ? 21 : pass == 1 ? 10 : 0;
         const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
         __syncthreads();
-        for (int i = tid; i < kSpBins; i += kSpThreads) hist[i] = 0;
+        for (int i = tid; i < kSpBins; i += NT) hist[i] = 0;
         __syncthreads();
 #pragma unroll 1
-        for (int q0 = 0; q0 < lim; q0 += kSpThreads) {
+        for (int q0 = 0; q0 < lim; q0 += NT) {
           const int q = q0 + tid;
           const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
           hist_add(hist, (c >> s2) & dmask, c != 0u && (c & pmask) == prefix);
         }
-        sp_rank_bin(hist, krem, red, found);
+        sp_rank_bin<NT>(hist, krem, red, found);
         prefix |= (uint32_t)found[0] << s2;
         pmask |= dmask << s2;
         krem -= found[1];
@@ -889,12 +897,12 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
     // emission in position order, 256 positions per round
     int run_gt = 0, run_eq = 0;
 #pragma unroll 1
-    for (int q0 = 0; q0 < lim; q0 += kSpThreads) {
+    for (int q0 = 0; q0 < lim; q0 += NT) {
       const int q = q0 + tid;
       const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
       const int g = c != 0u && c > tau, eq = c != 0u && c == tau;
       int total;
-      const int before = sp_scan_excl((g << 16) | eq, red, total);
+      const int before = sp_scan_excl<NT>((g << 16) | eq, red, total);
       const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
       if (g || (eq && eqb < need_eq)) out[gtb + min(eqb, need_eq)] = q;
       run_gt += total >> 16;
@@ -902,7 +910,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_select_kernel(TopkSplit
     }
   }
   __syncthreads();
-  for (int i = n_sel + tid; i < k; i += kSpThreads) out[i] = -1;
+  for (int i = n_sel + tid; i < k; i += NT) out[i] = -1;
   if (a.count && tid == 0) a.count[row] = n_sel;
 }
 
@@ -955,7 +963,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     topk_split_scan_kernel<<<dim3(sp.nchunk, (unsigned)rows), kSpThreads, 0, st>>>(sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    topk_split_select_kernel<<<(unsigned)rows, kSpThreads, 0, st>>>(sp);
+    topk_split_select_kernel<kSpSelThreads><<<(unsigned)rows, kSpSelThreads, 0, st>>>(sp);
     return hipGetLastError();
   }
   TopkRowArgs r{};
