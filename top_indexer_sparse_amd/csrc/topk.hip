@@ -484,11 +484,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
 //     rests on the sample.
 // ---------------------------------------------------------------------------
 constexpr int kSpChunk = 4096;
-constexpr int kSpThreads = 256;
+constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpPer = kSpChunk / kSpThreads;  // consecutive positions per thread
 constexpr int kSpRuns = 128, kSpRun = 16;      // the row sample: 2048 keys
 constexpr int kSpSamplePer = kSpRuns * kSpRun / kSpThreads;
+constexpr int kSpRunThreads = kSpThreads / kSpRuns;  // threads per sample run
+static_assert(kSpRunThreads * kSpSamplePer == kSpRun, "a run is split evenly over threads");
 constexpr int kSpBins = 2048;
 constexpr int kSpMaxRows = 128;    // rows of a launch taking the split path
 constexpr int kSpMinL = 8192;      // shortest row length taking it
@@ -616,10 +618,11 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
 #pragma unroll
     for (int i = 0; i < kSpPer; ++i) cs[i] = p0 + i < lim ? srow[p0 + i] : -INFINITY;
   }
-  // sample: run r = tid / 2 starts at r * lim / 128 (every position when the
+  // sample: run r = tid / kSpRunThreads starts at r * lim / 128 (every position when the
   // row is shorter than the sample)
   const int sbase = lim >= kSpRuns * kSpRun
-                        ? (int)((int64_t)(tid >> 1) * lim / kSpRuns) + kSpSamplePer * (tid & 1)
+                        ? (int)((int64_t)(tid / kSpRunThreads) * lim / kSpRuns) +
+                              kSpSamplePer * (tid % kSpRunThreads)
                         : kSpSamplePer * tid;
   float ss[kSpSamplePer];
 #pragma unroll
