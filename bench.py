@@ -97,7 +97,7 @@ def cpu_baseline(wl, budget_s=20.0):
             "kind": "oracle",
             "sample": f"{done} of {wl.B} sequences of {wl.name} (full L={wl.L}, k={wl.topk}, "
                       f"H={wl.H}), fp64 C oracle, OpenMP over (query, head) on {threads} "
-                      f"threads, {spent:.2f} s"}
+                      f"threads of {os.cpu_count()} ({cpu_model()}), {spent:.2f} s"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_32k_traffic.md")
@@ -153,6 +153,64 @@ def timed_after(step, fn, n, stream):
         e1.record(stream)
     torch.cuda.synchronize()
     return sum(e0.elapsed_time(e1) for e0, e1 in ev) / n
+
+
+def per_step_stats(step, n, stream, dev, flush_gib=1):
+    """Each step timed alone with HIP events, after an untimed pass that evicts
+    the 256 MB Infinity Cache: median, p10 and p90 of the step time in
+    microseconds (cold caches, unlike the back-to-back steps of the headline
+    number).  The pass reads flush_gib GiB of scratch (a sum), so that the
+    cache is left holding clean lines: a write pass would leave dirty ones
+    whose write-back the timed step would pay for."""
+    import torch
+    scratch = torch.ones(flush_gib << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        torch.sum(scratch, dim=0, out=sink)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    del scratch
+
+    def pct(p):
+        return us[min(n - 1, int(round(p * (n - 1))))]
+    return {"median_us": round(pct(0.5), 2), "p10_us": round(pct(0.1), 2),
+            "p90_us": round(pct(0.9), 2), "iters": n,
+            "cache_flush": f"{flush_gib} GiB scratch read before each step, not timed"}
+
+
+def copy_peak_gbs(dev, mib=1024, iters=5):
+    """Measured device-copy bandwidth: (bytes read + bytes written) / time of a
+    plain mib-MiB device-to-device copy, the practical HBM ceiling."""
+    import torch
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / iters
+    del src, dst
+    return 2 * (mib << 20) / sec / 1e9
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_probe(mib, dev):
@@ -236,6 +294,12 @@ def run_decode(args, api, dev):
         f"{idx_gbs:,.0f} GB/s algorithmic")
     log(f"sparse MLA {mla_ms * 1e3:.1f} us/launch incl. split combine, "
         f"{mla_tfs:,.0f} TFLOP/s, {mla_bytes / (mla_ms * 1e-3) / 1e9:,.0f} GB/s")
+    cold = per_step_stats(step, max(5, min(args.steps, 50)), stream, dev)
+    log(f"cold-cache step: median {cold['median_us']} us (p10 {cold['p10_us']}, "
+        f"p90 {cold['p90_us']})")
+    copy_gbs = copy_peak_gbs(dev)
+    log(f"device copy {copy_gbs:,.0f} GB/s (read + write); whole step "
+        f"{100 * per_q * qps / (copy_gbs * 1e9):.1f}% of it")
 
     result = {
         "metric": "decode queries/s at L=32K,k=2048; indexer+gather % of HBM roofline",
@@ -255,6 +319,9 @@ def run_decode(args, api, dev):
                    "indexer_keys": str(wl.k_idx.dtype).replace("torch.", "")},
         "hbm_frac_step": round(step_frac, 4),
         "bytes_per_query": per_q,
+        "copy_peak_gbs": round(copy_gbs, 1),
+        "hbm_frac_step_vs_copy": round(per_q * qps / (copy_gbs * 1e9), 4),
+        "per_step": cold,
         "roofline": {"bound": "hbm", "kernel": "indexer", "achieved": round(idx_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
