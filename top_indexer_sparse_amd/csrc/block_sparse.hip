@@ -15,6 +15,11 @@
 //  * block_pool_kernel: one work-group per (block, sequence); 8-byte bf16
 //    loads, fp32 sums.  A cache-maintenance step (the pooled keys of a block
 //    change only when the block fills), not part of a decode step.
+//  * block_score_kernel: one work-group per (64 blocks, KV head, sequence).
+//    Each pooled-key row (512 bytes) is read once, coalesced, by half a wave
+//    (16 bytes per lane) and scored against every query head of the KV group
+//    (or, with a shared choice, their sum); the per-lane partial dot products
+//    are summed over the half wave.  Scores go to the workspace, [B, Hq, nblk].
 //  * block_select_kernel: one work-group per (query head, sequence).  Block
 //    scores as (score key, inverted block index) keys, so that one maximum
 //    search orders by score with ties to the lower block; the nsel largest by
@@ -44,13 +49,15 @@ bool block_supported(const BlockArgs& a) {
          a.L / a.blk <= kBlkMaxBlocks;
 }
 
-// chosen blocks [B, Hq, nsel] int32
+// workspace: chosen blocks [B, Hq, nsel] int32 | block scores [B, Hq, L / blk] fp32
+static size_t block_chosen_bytes(int B, int Hq, int nsel) {
+  return ((size_t)B * Hq * nsel * sizeof(int32_t) + 255) & ~(size_t)255;
+}
 size_t block_workspace_bytes(int B, int Hq, int L, int nsel, int Hkv, int d, int blk) {
   (void)Hkv;
   (void)d;
-  (void)L;
-  if (blk < 1 || B < 0 || Hq < 1 || nsel < 1) return 0;
-  return (size_t)B * Hq * nsel * sizeof(int32_t);
+  if (blk < 1 || B < 0 || Hq < 1 || nsel < 1 || L < 0) return 0;
+  return block_chosen_bytes(B, Hq, nsel) + (size_t)B * Hq * (L / blk) * sizeof(float);
 }
 
 // ---------------------------------------------------------------------------
@@ -88,97 +95,158 @@ __device__ __forceinline__ uint32_t blk_score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-struct BlockSelArgs {
+struct BlockScoreArgs {
   const uint16_t* q;    // [B, Hq, d]
   const float* krep;    // [B, nblk, Hkv, d]
-  int Hq, Hkv, nblk, nsel;
+  int Hq, Hkv, nblk;
   int shared;           // score with the sum of the KV group's queries
+  float* scores;        // [B, Hq, nblk] (workspace)
+};
+
+constexpr int kScoreBlocks = 64;  // blocks per scoring work-group (16 per wave)
+
+// DPP lane moves (no LDS round trip): quad permutations and the row mirrors.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+// Sum over the 32 lanes of each half wave, in every lane: quad swaps, the
+// half-row and row mirrors (sum of 16), then rows 0 and 1 (2 and 3) swapped
+// by v_permlane16_swap.  Needs all 64 lanes active.
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += dpp_f32<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// G query heads per KV head.  Lane l of half-wave e holds dims 4 (l % 32) ..
+// +3 of each query; wave w scores blocks n0 + 16 w + 2 i + e, i < 8, all its
+// 16-byte loads issued before the first product.
+template <int G>
+__global__ __launch_bounds__(256) void block_score_kernel(BlockScoreArgs a) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int e = lane >> 5, l = lane & 31;
+  const int nblk = a.nblk;
+  float qv[G][4];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint2 u = *(const uint2*)(a.q + ((int64_t)b * a.Hq + g * G + hh) * kBlkD + 4 * l);
+    qv[hh][0] = bf16_lo(u.x);
+    qv[hh][1] = bf16_hi(u.x);
+    qv[hh][2] = bf16_lo(u.y);
+    qv[hh][3] = bf16_hi(u.y);
+  }
+  if (a.shared) {  // the group's summed query, heads in order
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[0][c] += qv[hh][c];
+  }
+  const int n0 = blockIdx.x * kScoreBlocks + 16 * wave + e;
+  float4 kv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = min(n0 + 2 * i, nblk - 1);
+    kv[i] = *(const float4*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD + 4 * l);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = n0 + 2 * i;
+    float p[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      p[hh] = 0.f;
+      if (a.shared && hh > 0) continue;  // uniform: one summed query
+      float acc = kv[i].x * qv[hh][0];
+      acc = fmaf(kv[i].y, qv[hh][1], acc);
+      acc = fmaf(kv[i].z, qv[hh][2], acc);
+      acc = fmaf(kv[i].w, qv[hh][3], acc);
+      p[hh] = half_wave_sum(acc);
+    }
+    if (n < nblk && l < G) {  // lane l of the half wave writes head g G + l
+      float v = p[0];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh)
+        if (!a.shared && l == hh) v = p[hh];
+      a.scores[((int64_t)b * a.Hq + g * G + l) * nblk + n] = v;
+    }
+  }
+}
+
+struct BlockSelArgs {
+  const float* scores;  // [B, Hq, nblk]
+  int Hq, nblk, nsel;
   int32_t* chosen;      // [B, Hq, nsel] (workspace)
   int32_t* blocks_out;  // [B, Hq, nsel] or null
 };
 
-// Largest 64-bit key over the wave (every lane gets it).
+// Largest 64-bit key over the wave (every lane gets it): quad swaps and row
+// mirrors give each row of 16 its maximum (DPP, both halves with the same
+// control), then the four row maxima through scalar registers.
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), o) << 32) |
-                       (uint32_t)__shfl_xor((int)(uint32_t)v, o);
-    v = w > v ? w : v;
+  v = max_u64(v, dpp_u64<0xb1>(v));
+  v = max_u64(v, dpp_u64<0x4e>(v));
+  v = max_u64(v, dpp_u64<0x141>(v));
+  v = max_u64(v, dpp_u64<0x140>(v));
+  uint64_t m = 0ull;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    m = max_u64(m, x);
   }
-  return v;
+  return m;
 }
 
-constexpr int kSelPerLane = kBlkMaxBlocks / 256;  // blocks per thread
+constexpr int kSelMaxPerLane = kBlkMaxBlocks / 256;  // blocks per thread, at most
 
 // One work-group per (query head, sequence).  Keys (score key << 32 | ~block)
 // order blocks by score, ties to the lower block, so the selection is a
 // plain maximum search: each wave takes the nsel largest keys of its share
 // (nsel rounds of a wave maximum, the winner's lane retiring it), one wave
 // then takes the nsel largest of the 4 nsel survivors the same way.
+template <int KPL>  // keys per thread: blocks n = tid + 256 r, r < KPL
 __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
   __shared__ uint64_t cand[4][kBlkMaxSel];
   __shared__ int pick[kBlkMaxSel];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
-  const int G = a.Hq / a.Hkv, g = h / G, nblk = a.nblk;
-  // the head's query, or with a shared choice the sum of the group's queries
-  // (the sum of the heads' block scores is the group-sum query's score, so
-  // the group's work-groups all reach the same choice), staged in LDS
-  __shared__ float qs[kBlkD];
-  if (tid < kBlkD) {
-    const int h0 = a.shared ? g * G : h, h1 = a.shared ? h0 + G : h + 1;
-    float acc = 0.f;
-    for (int hh = h0; hh < h1; ++hh)
-      acc += bf16_bits_to_float(a.q[((int64_t)b * a.Hq + hh) * kBlkD + tid]);
-    qs[tid] = acc;
-  }
-  __syncthreads();
-  float qf[kBlkD];
+  const int nblk = a.nblk;
+  const float* srow = a.scores + ((int64_t)b * a.Hq + h) * nblk;
+  // block n = tid + 256 r
+  uint64_t key[KPL];
 #pragma unroll
-  for (int i = 0; i < kBlkD / 4; ++i) {
-    const float4 v = *(const float4*)&qs[4 * i];
-    qf[4 * i] = v.x;
-    qf[4 * i + 1] = v.y;
-    qf[4 * i + 2] = v.z;
-    qf[4 * i + 3] = v.w;
-  }
-  // block n = tid + 256 r: one pooled-key row (512 bytes) per lane
-  uint64_t key[kSelPerLane];
-#pragma unroll
-  for (int r = 0; r < kSelPerLane; ++r) {
+  for (int r = 0; r < KPL; ++r) {
     const int n = tid + 256 * r;
     key[r] = 0ull;
     if (256 * r >= nblk) continue;  // uniform: nothing left for any thread
-    if (n < nblk) {
-      const float4* kr = (const float4*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD);
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {  // 8 x 16 bytes in flight
-        float4 v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = kr[8 * c + i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int d0 = 32 * c + 4 * i;
-          acc = fmaf(v[i].x, qf[d0], acc);
-          acc = fmaf(v[i].y, qf[d0 + 1], acc);
-          acc = fmaf(v[i].z, qf[d0 + 2], acc);
-          acc = fmaf(v[i].w, qf[d0 + 3], acc);
-        }
-      }
-      key[r] = ((uint64_t)blk_score_key(acc) << 32) | (uint32_t)~(uint32_t)n;
-    }
+    if (n < nblk) key[r] = ((uint64_t)blk_score_key(srow[n]) << 32) | (uint32_t)~(uint32_t)n;
   }
   // this wave's nsel largest keys
   const int m = min(nblk, a.nsel);
   for (int i = 0; i < m; ++i) {
     uint64_t best = 0ull;
 #pragma unroll
-    for (int r = 0; r < kSelPerLane; ++r) best = key[r] > best ? key[r] : best;
+    for (int r = 0; r < KPL; ++r) best = key[r] > best ? key[r] : best;
     const uint64_t w = wave_max_u64(best);
     if (lane == 0) cand[wave][i] = w;
     if (w != 0ull) {  // the owner retires the winning key (keys are distinct)
 #pragma unroll
-      for (int r = 0; r < kSelPerLane; ++r) key[r] = key[r] == w ? 0ull : key[r];
+      for (int r = 0; r < KPL; ++r) key[r] = key[r] == w ? 0ull : key[r];
     }
   }
   __syncthreads();
@@ -423,17 +491,43 @@ hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d, int bl
 hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int nblk = a.L / a.blk;
+  float* scores = (float*)((char*)a.ws + block_chosen_bytes(a.B, a.Hq, a.nsel));
+  if (nblk > 0) {
+    BlockScoreArgs c{};
+    c.q = (const uint16_t*)a.q;
+    c.krep = a.krep;
+    c.Hq = a.Hq;
+    c.Hkv = a.Hkv;
+    c.nblk = nblk;
+    c.shared = a.shared_choice;
+    c.scores = scores;
+    const dim3 grid((unsigned)((nblk + kScoreBlocks - 1) / kScoreBlocks), (unsigned)a.Hkv,
+                    (unsigned)a.B);
+    switch (a.Hq / a.Hkv) {
+      case 1: block_score_kernel<1><<<grid, 256, 0, st>>>(c); break;
+      case 2: block_score_kernel<2><<<grid, 256, 0, st>>>(c); break;
+      case 4: block_score_kernel<4><<<grid, 256, 0, st>>>(c); break;
+      default: block_score_kernel<8><<<grid, 256, 0, st>>>(c); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   BlockSelArgs s{};
-  s.q = (const uint16_t*)a.q;
-  s.krep = a.krep;
+  s.scores = scores;
   s.Hq = a.Hq;
-  s.Hkv = a.Hkv;
   s.nblk = nblk;
   s.nsel = a.nsel;
-  s.shared = a.shared_choice;
   s.chosen = (int32_t*)a.ws;
   s.blocks_out = a.blocks_out;
-  block_select_kernel<<<dim3(a.Hq, a.B), 256, 0, st>>>(s);
+  const dim3 sgrid((unsigned)a.Hq, (unsigned)a.B);
+  if (nblk <= 256 * 4)
+    block_select_kernel<4><<<sgrid, 256, 0, st>>>(s);
+  else if (nblk <= 256 * 8)
+    block_select_kernel<8><<<sgrid, 256, 0, st>>>(s);
+  else if (nblk <= 256 * 16)
+    block_select_kernel<16><<<sgrid, 256, 0, st>>>(s);
+  else
+    block_select_kernel<kSelMaxPerLane><<<sgrid, 256, 0, st>>>(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   BlockAttnArgs t{};
