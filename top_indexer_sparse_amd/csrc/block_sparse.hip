@@ -27,10 +27,9 @@
 //    written in ascending block order.
 //  * block_attn_kernel: one work-group per (query head, sequence).  The
 //    visible ranges (sinks, chosen blocks, window) are merged into disjoint
-//    ascending ranges; the four waves take 64-token chunks in turn: lane =
-//    token for q . k (the key row is one lane's 256 contiguous bytes), lane =
-//    dimension pair for the value sum (the value row is one coalesced 256-byte
-//    load per token), with an online softmax per wave and a final merge.
+//    ascending ranges; the four waves take 64-token chunks in turn.  Sixteen
+//    lanes share each key and value row (16 bytes each, four rows per load
+//    instruction), with an online softmax per wave and a final merge.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -189,9 +188,11 @@ struct BlockSelArgs {
   int32_t* blocks_out;  // [B, Hq, nsel] or null
 };
 
-// Largest 64-bit key over the wave (every lane gets it): quad swaps and row
+// Largest 64-bit key over the wave, in every lane: quad swaps and row
 // mirrors give each row of 16 its maximum (DPP, both halves with the same
-// control), then the four row maxima through scalar registers.
+// control), then gfx950's permlane16 / permlane32 swaps exchange rows (each
+// swap hands a lane the pair {v[l], v[l ^ 16]}, then {v[l], v[l ^ 32]}, the
+// two 32-bit halves taken from the same lanes).  Needs all 64 lanes active.
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
@@ -202,14 +203,21 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   v = max_u64(v, dpp_u64<0x4e>(v));
   v = max_u64(v, dpp_u64<0x141>(v));
   v = max_u64(v, dpp_u64<0x140>(v));
-  uint64_t m = 0ull;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 16 * r) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
-    m = max_u64(m, x);
+  {
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    v = max_u64(((uint64_t)(uint32_t)h[0] << 32) | (uint32_t)l[0],
+                ((uint64_t)(uint32_t)h[1] << 32) | (uint32_t)l[1]);
   }
-  return m;
+  {
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    v = max_u64(((uint64_t)(uint32_t)h[0] << 32) | (uint32_t)l[0],
+                ((uint64_t)(uint32_t)h[1] << 32) | (uint32_t)l[1]);
+  }
+  return v;
 }
 
 constexpr int kSelMaxPerLane = kBlkMaxBlocks / 256;  // blocks per thread, at most
@@ -228,13 +236,15 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
   const int nblk = a.nblk;
   const float* srow = a.scores + ((int64_t)b * a.Hq + h) * nblk;
   // block n = tid + 256 r
+  // All loads are issued before any is used (clamped addresses, masked keys).
+  float sv[KPL];
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) sv[r] = srow[min(tid + 256 * r, nblk - 1)];
   uint64_t key[KPL];
 #pragma unroll
   for (int r = 0; r < KPL; ++r) {
     const int n = tid + 256 * r;
-    key[r] = 0ull;
-    if (256 * r >= nblk) continue;  // uniform: nothing left for any thread
-    if (n < nblk) key[r] = ((uint64_t)blk_score_key(srow[n]) << 32) | (uint32_t)~(uint32_t)n;
+    key[r] = n < nblk ? ((uint64_t)blk_score_key(sv[r]) << 32) | (uint32_t)~(uint32_t)n : 0ull;
   }
   // this wave's nsel largest keys
   const int m = min(nblk, a.nsel);
@@ -244,10 +254,10 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
     for (int r = 0; r < KPL; ++r) best = key[r] > best ? key[r] : best;
     const uint64_t w = wave_max_u64(best);
     if (lane == 0) cand[wave][i] = w;
-    if (w != 0ull) {  // the owner retires the winning key (keys are distinct)
+    // the owner retires the winning key (keys are distinct; a zero winner
+    // leaves only zero keys, which stay zero)
 #pragma unroll
-      for (int r = 0; r < KPL; ++r) key[r] = key[r] == w ? 0ull : key[r];
-    }
+    for (int r = 0; r < KPL; ++r) key[r] = key[r] == w ? 0ull : key[r];
   }
   __syncthreads();
   if (wave == 0) {
@@ -293,17 +303,18 @@ struct BlockAttnArgs {
   const uint16_t* k;  // [B, L, Hkv, d]
   const uint16_t* v;
   const int32_t* chosen;  // [B, Hq, nsel], ascending, -1 padded
-  int L, Hq, Hkv, blk, nsel, n_sink, n_win;
+  int B, L, Hq, Hkv, blk, nsel, n_sink, n_win;
   float scale_log2;
   float* out;  // [B, Hq, d]
 };
 
-__device__ __forceinline__ float wave_max_f(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Sum over the 16 lanes of each row (quad swaps and the row mirrors), in
+// every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xb1>(v);
+  v += dpp_f32<0x4e>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
   return v;
 }
 
@@ -311,25 +322,33 @@ __global__ __launch_bounds__(256) void block_attn_kernel(BlockAttnArgs a) {
   __shared__ int rs[kBlkMaxRanges], re[kBlkMaxRanges], rcum[kBlkMaxRanges + 1];
   __shared__ int st[kBlkMaxRanges], en[kBlkMaxRanges];  // unsorted ranges
   __shared__ int s_nr;
-  __shared__ float pb[4][64];
+  __shared__ int chs[kBlkMaxSel];
   __shared__ int tb[4][64];
   __shared__ float wm[4], wl[4];
   __shared__ float wo[4][kBlkD];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  // Work-groups go to the eight XCDs in turn (linear id mod 8).  Item
+  // w = (sequence, head) is placed so that each XCD takes a contiguous run
+  // of items: a KV group's query heads then share one L2, where the keys and
+  // values they have in common (sinks, window, blocks chosen alike) are read
+  // from HBM once.
+  const int n_items = a.Hq * a.B, id = blockIdx.x;
+  const int w_item = n_items % 8 == 0 ? (id % 8) * (n_items / 8) + id / 8 : id;
+  const int h = w_item % a.Hq, b = w_item / a.Hq, tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
   const int g = h / (a.Hq / a.Hkv);
   const int L = a.L;
 
   // ---- visible ranges: sinks, chosen blocks, window -> disjoint, ascending
+  if (tid < a.nsel) chs[tid] = a.chosen[((int64_t)b * a.Hq + h) * a.nsel + tid];
+  __syncthreads();
   if (tid == 0) {
     int n = 0;
     if (a.n_sink > 0) {
       st[n] = 0;
       en[n++] = min(a.n_sink, L);
     }
-    const int32_t* ch = a.chosen + ((int64_t)b * a.Hq + h) * a.nsel;
     for (int i = 0; i < a.nsel; ++i) {
-      const int c = ch[i];
+      const int c = chs[i];
       if (c < 0) break;
       st[n] = c * a.blk;
       en[n++] = c * a.blk + a.blk;
@@ -367,97 +386,108 @@ __global__ __launch_bounds__(256) void block_attn_kernel(BlockAttnArgs a) {
     rcum[nr] = cum;
     s_nr = nr;
   }
-  // query in registers, fp32 (every lane holds the whole row)
-  float qf[kBlkD];
+  // Lane (r, j) = (lane / 16, lane % 16) takes dims 8 j .. 8 j + 7 of slot
+  // 4 i + r, i < 16, of each 64-slot chunk: every key or value row (256
+  // bytes) is read by 16 lanes with one 16-byte load each, four rows per
+  // instruction.  A score is summed over its 16 lanes by DPP moves, so the
+  // row's lanes all hold it; the softmax state and the value sums stay in
+  // registers, and the four rows' partial sums are added at the end.
+  const int r4 = lane >> 4, j16 = lane & 15;
+  float qd[8];
   {
-    const uint4* qp = (const uint4*)(a.q + ((int64_t)b * a.Hq + h) * kBlkD);
-#pragma unroll
-    for (int i = 0; i < kBlkD / 8; ++i) {
-      const uint4 u = qp[i];
-      qf[8 * i + 0] = bf16_lo(u.x);
-      qf[8 * i + 1] = bf16_hi(u.x);
-      qf[8 * i + 2] = bf16_lo(u.y);
-      qf[8 * i + 3] = bf16_hi(u.y);
-      qf[8 * i + 4] = bf16_lo(u.z);
-      qf[8 * i + 5] = bf16_hi(u.z);
-      qf[8 * i + 6] = bf16_lo(u.w);
-      qf[8 * i + 7] = bf16_hi(u.w);
-    }
+    const uint4 u = *(const uint4*)(a.q + ((int64_t)b * a.Hq + h) * kBlkD + 8 * j16);
+    qd[0] = bf16_lo(u.x);
+    qd[1] = bf16_hi(u.x);
+    qd[2] = bf16_lo(u.y);
+    qd[3] = bf16_hi(u.y);
+    qd[4] = bf16_lo(u.z);
+    qd[5] = bf16_hi(u.z);
+    qd[6] = bf16_lo(u.w);
+    qd[7] = bf16_hi(u.w);
   }
   __syncthreads();
   const int nr = s_nr, ntok = rcum[nr];
   const int64_t row_stride = (int64_t)a.Hkv * kBlkD;  // elements between tokens
-  const uint16_t* kb = a.k + (int64_t)b * L * row_stride + (int64_t)g * kBlkD;
-  const uint16_t* vb = a.v + (int64_t)b * L * row_stride + (int64_t)g * kBlkD;
+  const uint16_t* kb = a.k + (int64_t)b * L * row_stride + (int64_t)g * kBlkD + 8 * j16;
+  const uint16_t* vb = a.v + (int64_t)b * L * row_stride + (int64_t)g * kBlkD + 8 * j16;
 
-  float m_w = -INFINITY, l_w = 0.f, o0 = 0.f, o1 = 0.f;  // dims 2 lane, 2 lane + 1
+  float m_w = -INFINITY, l_w = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // dims 8 j .. + 7, this row's slots
   for (int c = wave; 64 * c < ntok; c += 4) {
-    const int t = 64 * c + lane;
-    const bool valid = t < ntok;
-    int tok = 0;
-    if (valid) {  // range holding flattened index t (binary search over rcum)
-      int lo = 0, hi = nr - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (rcum[mid] <= t) lo = mid;
-        else hi = mid - 1;
+    {  // token of slot 64 c + lane (binary search over the ranges' offsets)
+      const int t = 64 * c + lane;
+      int tok = 0;
+      if (t < ntok) {
+        int lo = 0, hi = nr - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (rcum[mid] <= t) lo = mid;
+          else hi = mid - 1;
+        }
+        tok = rs[lo] + (t - rcum[lo]);
       }
-      tok = rs[lo] + (t - rcum[lo]);
+      tb[wave][lane] = tok;  // past the end: token 0 (read, then masked)
     }
-    float s = -INFINITY;
-    if (valid) {
-      const uint4* kp = (const uint4*)(kb + (int64_t)tok * row_stride);
-      uint4 kr[kBlkD / 8];
+    __builtin_amdgcn_wave_barrier();
+    int tokr[16];
 #pragma unroll
-      for (int i = 0; i < kBlkD / 8; ++i) kr[i] = kp[i];
-      float acc = 0.f;
+    for (int i = 0; i < 16; ++i) tokr[i] = tb[wave][4 * i + r4];
+    uint4 kr[16];
 #pragma unroll
-      for (int i = 0; i < kBlkD / 8; ++i) {
-        acc = fmaf(qf[8 * i + 0], bf16_lo(kr[i].x), acc);
-        acc = fmaf(qf[8 * i + 1], bf16_hi(kr[i].x), acc);
-        acc = fmaf(qf[8 * i + 2], bf16_lo(kr[i].y), acc);
-        acc = fmaf(qf[8 * i + 3], bf16_hi(kr[i].y), acc);
-        acc = fmaf(qf[8 * i + 4], bf16_lo(kr[i].z), acc);
-        acc = fmaf(qf[8 * i + 5], bf16_hi(kr[i].z), acc);
-        acc = fmaf(qf[8 * i + 6], bf16_lo(kr[i].w), acc);
-        acc = fmaf(qf[8 * i + 7], bf16_hi(kr[i].w), acc);
-      }
-      s = acc * a.scale_log2;
+    for (int i = 0; i < 16; ++i) kr[i] = *(const uint4*)(kb + (int64_t)tokr[i] * row_stride);
+    float sc[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = qd[0] * bf16_lo(kr[i].x);
+      acc = fmaf(qd[1], bf16_hi(kr[i].x), acc);
+      acc = fmaf(qd[2], bf16_lo(kr[i].y), acc);
+      acc = fmaf(qd[3], bf16_hi(kr[i].y), acc);
+      acc = fmaf(qd[4], bf16_lo(kr[i].z), acc);
+      acc = fmaf(qd[5], bf16_hi(kr[i].z), acc);
+      acc = fmaf(qd[6], bf16_lo(kr[i].w), acc);
+      acc = fmaf(qd[7], bf16_hi(kr[i].w), acc);
+      acc = row16_sum(acc);
+      sc[i] = 64 * c + 4 * i + r4 < ntok ? acc * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
     }
-    const float cmax = wave_max_f(s);  // finite: the chunk has a valid token
+    uint4 vr[16];  // value rows, loaded while the softmax runs
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vr[i] = *(const uint4*)(vb + (int64_t)tokr[i] * row_stride);
+    const float cmax = max_over_lane_groups_vx(mx);  // finite: the chunk has a valid slot
     const float m_new = fmaxf(m_w, cmax);
     const float alpha = __builtin_amdgcn_exp2f(m_w - m_new);  // 0 at the first chunk
-    const float p = valid ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
-    l_w = l_w * alpha + wave_sum_f(p);
-    o0 *= alpha;
-    o1 *= alpha;
-    m_w = m_new;
-    pb[wave][lane] = p;
-    tb[wave][lane] = tok;
-    __builtin_amdgcn_wave_barrier();
-    // value rows: 32 coalesced 256-byte loads in flight at a time
+    float psum = 0.f;
 #pragma unroll
-    for (int t0 = 0; t0 < 64; t0 += 32) {
-      uint32_t vv[32];
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        vv[i] = *(const uint32_t*)(vb + (int64_t)tb[wave][t0 + i] * row_stride + 2 * lane);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float pp = pb[wave][t0 + i];
-        o0 = fmaf(pp, bf16_lo(vv[i]), o0);
-        o1 = fmaf(pp, bf16_hi(vv[i]), o1);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sc[i] - m_new);  // 0 for masked slots
+      psum += p;
+      o[0] = fmaf(p, bf16_lo(vr[i].x), o[0]);
+      o[1] = fmaf(p, bf16_hi(vr[i].x), o[1]);
+      o[2] = fmaf(p, bf16_lo(vr[i].y), o[2]);
+      o[3] = fmaf(p, bf16_hi(vr[i].y), o[3]);
+      o[4] = fmaf(p, bf16_lo(vr[i].z), o[4]);
+      o[5] = fmaf(p, bf16_hi(vr[i].z), o[5]);
+      o[6] = fmaf(p, bf16_lo(vr[i].w), o[6]);
+      o[7] = fmaf(p, bf16_hi(vr[i].w), o[7]);
     }
-    __builtin_amdgcn_wave_barrier();  // pb / tb are rewritten by the next chunk
+    l_w = l_w * alpha + sum_over_lane_groups_vx(psum);
+    m_w = m_new;
+    __builtin_amdgcn_wave_barrier();  // tb is rewritten by the next chunk
   }
-  // ---- merge the four waves' (m, l, o)
+  // ---- the four rows' partial value sums, then merge the four waves' (m, l, o)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = sum_over_lane_groups_vx(o[e]);
   if (lane == 0) {
     wm[wave] = m_w;
     wl[wave] = l_w;
   }
-  wo[wave][2 * lane] = o0;
-  wo[wave][2 * lane + 1] = o1;
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wo[wave][8 * lane + e] = o[e];
+  }
   __syncthreads();
   if (wave == 0) {
     float M = -INFINITY;
@@ -471,9 +501,9 @@ __global__ __launch_bounds__(256) void block_attn_kernel(BlockAttnArgs a) {
       n1 += e * wo[w][2 * lane + 1];
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    float* o = a.out + ((int64_t)b * a.Hq + h) * kBlkD;
-    o[2 * lane] = n0 * inv;
-    o[2 * lane + 1] = n1 * inv;
+    float* out = a.out + ((int64_t)b * a.Hq + h) * kBlkD;
+    out[2 * lane] = n0 * inv;
+    out[2 * lane + 1] = n1 * inv;
   }
 }
 
@@ -535,6 +565,7 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   t.k = (const uint16_t*)a.k;
   t.v = (const uint16_t*)a.v;
   t.chosen = s.chosen;
+  t.B = a.B;
   t.L = a.L;
   t.Hq = a.Hq;
   t.Hkv = a.Hkv;
@@ -544,7 +575,7 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   t.n_win = a.n_win;
   t.scale_log2 = a.sm_scale * kLog2e;
   t.out = a.out;
-  block_attn_kernel<<<dim3(a.Hq, a.B), 256, 0, st>>>(t);
+  block_attn_kernel<<<dim3((unsigned)(a.Hq * a.B)), 256, 0, st>>>(t);
   return hipGetLastError();
 }
 
