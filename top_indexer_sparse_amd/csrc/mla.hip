@@ -555,7 +555,40 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
                                                           int nsplit, int dc,
                                                           float* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const int64_t u = blockIdx.x;  // (bt, h)
+  // (bt, h), laid out over the XCDs as the MLA kernel lays out its blocks
+  // (blocks go to the 8 XCDs round-robin; each XCD takes a contiguous run of
+  // queries), so the partials are read from the L2 that they were written to
+  int64_t u = blockIdx.x;
+  if ((gridDim.x & 7) == 0) u = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  constexpr int kPre = 8;
+  if (dc == 4 * 128 && nsplit <= kPre) {
+    // every load first (clamped split index, zero weight past nsplit), so the
+    // work-group waits for one memory round trip instead of three
+    float2 ml[kPre];
+    floatx4 po[kPre];
+#pragma unroll
+    for (int s = 0; s < kPre; ++s) {
+      const int64_t us = u * nsplit + min(s, nsplit - 1);
+      ml[s] = *(const float2*)(part_ml + 2 * us);
+      po[s] = *(const floatx4*)(part_o + us * dc + 4 * threadIdx.x);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kPre; ++s) M = s < nsplit ? fmaxf(M, ml[s].x) : M;
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float Lsum = 0.f;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kPre; ++s) {
+      const float wgt = s < nsplit ? exp2f(ml[s].x - Mu) : 0.f;
+      Lsum += wgt * ml[s].y;
+      acc += wgt * po[s];
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    *(floatx4*)(out + u * dc + 4 * threadIdx.x) = acc * inv;
+    if (lse && threadIdx.x == 0) lse[u] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : -INFINITY;
+    return;
+  }
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[2 * (u * nsplit + s)]);
   const float Mu = M == -INFINITY ? 0.f : M;
