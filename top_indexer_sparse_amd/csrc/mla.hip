@@ -548,6 +548,40 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   }
 }
 
+// Merge of (query, head) u's nsplit <= NS partials, 512 dims, 128 threads:
+// every load first (clamped split index, zero weight past nsplit), so the
+// work-group waits for one memory round trip instead of three.
+template <int NS>
+__device__ __forceinline__ void mla_combine_small(const float* __restrict__ part_o,
+                                                  const float* __restrict__ part_ml, int nsplit,
+                                                  int64_t u, float* __restrict__ out,
+                                                  float* __restrict__ lse) {
+  constexpr int dc = 4 * 128;
+  float2 ml[NS];
+  floatx4 po[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int64_t us = u * nsplit + min(s, nsplit - 1);
+    ml[s] = *(const float2*)(part_ml + 2 * us);
+    po[s] = *(const floatx4*)(part_o + us * dc + 4 * threadIdx.x);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) M = s < nsplit ? fmaxf(M, ml[s].x) : M;
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float Lsum = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float wgt = s < nsplit ? exp2f(ml[s].x - Mu) : 0.f;
+    Lsum += wgt * ml[s].y;
+    acc += wgt * po[s];
+  }
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  *(floatx4*)(out + u * dc + 4 * threadIdx.x) = acc * inv;
+  if (lse && threadIdx.x == 0) lse[u] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : -INFINITY;
+}
+
 // Merge nsplit partial (m, l, o) of one (query, head): one 128-thread group,
 // four output columns per thread.
 __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
@@ -560,34 +594,10 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
   // queries), so the partials are read from the L2 that they were written to
   int64_t u = blockIdx.x;
   if ((gridDim.x & 7) == 0) u = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  constexpr int kPre = 8;
-  if (dc == 4 * 128 && nsplit <= kPre) {
-    // every load first (clamped split index, zero weight past nsplit), so the
-    // work-group waits for one memory round trip instead of three
-    float2 ml[kPre];
-    floatx4 po[kPre];
-#pragma unroll
-    for (int s = 0; s < kPre; ++s) {
-      const int64_t us = u * nsplit + min(s, nsplit - 1);
-      ml[s] = *(const float2*)(part_ml + 2 * us);
-      po[s] = *(const floatx4*)(part_o + us * dc + 4 * threadIdx.x);
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kPre; ++s) M = s < nsplit ? fmaxf(M, ml[s].x) : M;
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float Lsum = 0.f;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kPre; ++s) {
-      const float wgt = s < nsplit ? exp2f(ml[s].x - Mu) : 0.f;
-      Lsum += wgt * ml[s].y;
-      acc += wgt * po[s];
-    }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    *(floatx4*)(out + u * dc + 4 * threadIdx.x) = acc * inv;
-    if (lse && threadIdx.x == 0) lse[u] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : -INFINITY;
-    return;
+  if (dc == 4 * 128) {  // uniform
+    if (nsplit <= 4) return mla_combine_small<4>(part_o, part_ml, nsplit, u, out, lse);
+    if (nsplit <= 8) return mla_combine_small<8>(part_o, part_ml, nsplit, u, out, lse);
+    if (nsplit <= 16) return mla_combine_small<16>(part_o, part_ml, nsplit, u, out, lse);
   }
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[2 * (u * nsplit + s)]);
