@@ -200,7 +200,9 @@ def test_mla_fp32_vector_path():
     assert err < 1e-4  # fp32 arithmetic
 
 
-@pytest.mark.parametrize("B,k,H", [(2, 2048, 128), (5, 300, 64), (40, 96, 128)])
+# KV splits per (query, 64-head group): 32, 4, 2 and 8 -- the split combine's
+# general path and its load-first paths for up to 4 and 8 splits
+@pytest.mark.parametrize("B,k,H", [(2, 2048, 128), (5, 300, 64), (40, 96, 128), (16, 600, 128)])
 def test_mla_bf16_mfma(B, k, H):
     _announce(f"mla bf16 B={B} k={k} H={H}")
     L = 2600

@@ -146,6 +146,40 @@ __device__ __forceinline__ void dma16_addr(const uint8_t* gaddr, uint32_t lds_ba
                : "s"(lds_base), "v"(gaddr)
                : "memory", "m0");
 }
+// Four wave-wide global->LDS loads behind one M0 write: load e (e < 4) copies
+// lane l's 16 bytes at gbase + v_e to LDS byte lds_base + 1024 e + 16 l.  The
+// instruction offset 1024 e moves both the global and the LDS address, so it
+// is taken back out of the per-lane offset; the SGPR base is lowered by 4096
+// and every offset raised by as much, so that no offset wraps (callers keep
+// v_e + 4096 below 2^32).  Four copies with one M0 write leave the issuing
+// wave sooner than four separately issued ones.
+__device__ __forceinline__ void dma16x4(const uint8_t* gbase, uint32_t v0, uint32_t v1,
+                                        uint32_t v2, uint32_t v3, uint32_t lds_base) {
+  const uint8_t* gb = gbase - 4096;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072"
+      :
+      : "s"(lds_base), "v"(v0 + 4096u), "v"(v1 + 3072u), "v"(v2 + 2048u), "v"(v3 + 1024u), "s"(gb)
+      : "memory", "m0");
+}
+// The same with full 64-bit per-lane addresses.
+__device__ __forceinline__ void dma16x4_addr(const uint8_t* a0, const uint8_t* a1,
+                                             const uint8_t* a2, const uint8_t* a3,
+                                             uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, off offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, off offset:3072"
+      :
+      : "s"(lds_base), "v"(a0), "v"(a1 - 1024), "v"(a2 - 2048), "v"(a3 - 3072)
+      : "memory", "m0");
+}
 // One wave-wide global->LDS load of 4 bytes per lane: lane l's dword at
 // gbase + voff lands at LDS byte lds_base + 4 l.
 __device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint32_t lds_base) {

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   // [0, L) fetches row 0 and is masked out of the softmax.
   const int ntiles = (nslots + kMlaTile - 1) / kMlaTile;
 
-  // ---- tile fetch: wave w < NH issues the 1 KB pieces q = w, w + NH, ... ----
+  // ---- tile fetch: wave w < NH issues the 1 KB pieces q = NLD w .. NLD w + NLD - 1 ----
   // Lane l of load i fills 16-byte slot c = 64 q + l of the tile: row c / 72,
   // position c % 72, which holds piece (c % 72) ^ swz(row).  Rows and pieces
   // are the same for every tile, so they are computed once; per load only the
@@ -215,15 +215,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
   uint32_t drow[NLD], dpiece[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int c = 64 * (wv + NH * i) + lane;
+    const int c = 64 * (NLD * wv + i) + lane;
     const int r = c / kMlaPieces, pp = c % kMlaPieces;
     drow[i] = 4 * r;                  // byte offset into a tile's slice of spos
     dpiece[i] = 16 * (pp ^ row_swz(r));
   }
   // Loads I0 <= i < I1 of this wave's share of tile tl.  A tile's loads are
-  // issued in three parts spread over the previous tile's compute: the CU's
-  // address unit takes one 1 KB load per ~16 cycles, so the four waves'
-  // 36 loads issued back to back would stall every wave for ~600 cycles.
+  // issued in three parts spread over the previous tile's compute (each load
+  // holds its wave at issue while the memory pipeline is busy), four at a
+  // time behind one M0 write where the part allows.
   auto issue_part = [&](int tl, auto I0c, auto I1c) {
     constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
     if (!issuer) return;
@@ -241,29 +241,38 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_mfma_kernel(MlaKernelArgs a) {
         srow[i] = *(const uint32_t*)(sp + drow[i]);
       }
     }
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
+    auto voff = [&](int i) {  // packed layout: per-lane byte offset from cb
       const uint32_t s = srow[i] < nrows ? srow[i] : 0u;  // skipped slot: row 0
-      const uint32_t ldst = dst + 1024u * (uint32_t)(wv + NH * i);
-      if constexpr (PACKED) {
-        dma16(cb, s * (uint32_t)a.c_stride_b + dpiece[i], ldst);
-      } else {
-        const bool rope = dpiece[i] >= 1024u;
-        const uint8_t* src;
-        if (rope)
-          src = a.zero_rope ? g_mla_zero + (dpiece[i] & 1023u)
-                            : rb + (s * (uint32_t)a.r_stride_b + (dpiece[i] & 1023u));
-        else if (s < (uint32_t)a.L)
-          src = cb + (s * (uint32_t)a.c_stride_b + dpiece[i]);
+      return s * (uint32_t)a.c_stride_b + dpiece[i];
+    };
+    auto src = [&](int i) {  // split layout: per-lane address
+      const uint32_t s = srow[i] < nrows ? srow[i] : 0u;
+      if (dpiece[i] >= 1024u)
+        return a.zero_rope ? g_mla_zero + (dpiece[i] & 1023u)
+                           : rb + (s * (uint32_t)a.r_stride_b + (dpiece[i] & 1023u));
+      if (s < (uint32_t)a.L) return cb + (s * (uint32_t)a.c_stride_b + dpiece[i]);
+      return wb + ((s - (uint32_t)a.L) * (uint32_t)a.win_stride_b + dpiece[i]);
+    };
+    static_for<I0, I1>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const uint32_t ldst = dst + 1024u * (uint32_t)(NLD * wv + i);
+      if constexpr ((i - I0) % 4 == 0 && i + 4 <= I1) {  // a group of four
+        if constexpr (PACKED)
+          dma16x4(cb, voff(i), voff(i + 1), voff(i + 2), voff(i + 3), ldst);
         else
-          src = wb + ((s - (uint32_t)a.L) * (uint32_t)a.win_stride_b + dpiece[i]);
-        dma16_addr(src, ldst);
+          dma16x4_addr(src(i), src(i + 1), src(i + 2), src(i + 3), ldst);
+      } else if constexpr ((i - I0) / 4 * 4 + 4 > I1 - I0) {  // past the last group
+        if constexpr (PACKED)
+          dma16(cb, voff(i), ldst);
+        else
+          dma16_addr(src(i), ldst);
       }
-    }
+    });
   };
+  static_assert(NLD == 9, "parts of 4, 4 and 1 loads");
   using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, NLD / 3>;
-  using P2 = std::integral_constant<int, 2 * NLD / 3>;
+  using P1 = std::integral_constant<int, 4>;
+  using P2 = std::integral_constant<int, 8>;
   using P3 = std::integral_constant<int, NLD>;
   auto issue = [&](int tl) { issue_part(tl, P0{}, P3{}); };
 
@@ -765,7 +774,9 @@ bool mla_uses_mfma(const MlaArgs& a) {
 bool mla_supported(const MlaArgs& a) {
   // the bf16 path addresses a sequence's rows with 32-bit byte offsets
   if (mla_uses_mfma(a))
-    return (int64_t)a.L * a.c_stride * 2 < (1LL << 32) && (int64_t)a.L * a.r_stride * 2 < (1LL << 32) &&
+    // (with 8 KB to spare: grouped copies raise the offsets by up to 4 KB)
+    return (int64_t)a.L * a.c_stride * 2 < (1LL << 32) - 8192 &&
+           (int64_t)a.L * a.r_stride * 2 < (1LL << 32) - 8192 &&
            (int64_t)a.n_win * a.win_stride * 2 < (1LL << 32) && (a.n_win == 0 || a.zero_rope) &&
            (a.dense == 0 || (a.k == a.L && a.n_win == 0));
   if (a.n_win || a.zero_rope || a.dense) return false;  // bf16 MFMA path only
