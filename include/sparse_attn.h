@@ -159,7 +159,7 @@ int sparse_attn_topk(const float* scores, const int32_t* q_pos,
  * A query whose slots are all skipped gets out = 0 and lse = -inf.
  * Compiled set: fp32 path dc <= 512, dR <= 64, H * dc <= 8192; bf16 path
  * (dc, dR) = (512, 64), H a multiple of 64, and one sequence's rows within
- * 4 GiB (L * row stride * 2 bytes < 2^32).  k >= 1.
+ * 4 GiB less 8 KiB (L * row stride * 2 bytes < 2^32 - 8192).  k >= 1.
  * ws: sparse_attn_workspace_bytes(SA_OP_MLA_FORWARD, B, T, L, k, H, dc).
  * ------------------------------------------------------------------------- */
 int sparse_attn_mla_forward(const void* q_lat, const void* q_rope, int q_dtype,
