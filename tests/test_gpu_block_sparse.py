@@ -122,6 +122,17 @@ def test_block_sparse_fewer_blocks_than_nsel():
     _run_case(wl)
 
 
+@pytest.mark.parametrize("L,blk,nsel", [(131109, 64, 64), (262144, 32, 40)])
+def test_block_sparse_long_rows_and_max_nsel(L, blk, nsel):
+    # 2048 and 8192 blocks per row (the selection's 8- and 32-keys-per-thread
+    # variants), the largest nsel, a ragged tail; one KV group, B * Hq = 4
+    # attention work-groups (fewer than the XCDs: no XCD layout)
+    _announce(f"block sparse L={L} blk={blk} nsel={nsel}")
+    wl = workloads.block_sparse_64k(B=1, L=L, Hq=4, Hkv=1, blk=blk, nsel=nsel, n_sink=32,
+                                    n_win=300)
+    _run_case(wl)
+
+
 def test_block_sparse_fullsize_sampled():
     """The block-sparse workload at full size (B=16, L=65536, 32/8 heads,
     block 64, top 16 + 64 sinks + 512 window); two sequences go to the oracle."""
