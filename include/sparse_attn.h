@@ -304,7 +304,8 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w,
  * Compiled set: d = 128, blk in {32, 64, 128}, Hq / Hkv in {1, 2, 4, 8},
  * 1 <= nsel <= 64, L / blk <= 8192.
  * ws: sparse_attn_workspace_bytes(SA_OP_BLOCK_DECODE, B, Hq, L, nsel, Hkv, d)
- *   (the chosen blocks, [B, Hq, nsel] int32).
+ *   (the block scores, [B, Hq, L / blk] fp32, sized for blk = 32; may be
+ *   NULL when that is 0 bytes).
  * Errors as for the other entry points; a query head whose visible set is
  * empty (L < blk, no sinks, no window) gets out = 0.
  * ------------------------------------------------------------------------- */

@@ -20,16 +20,15 @@
 //    (16 bytes per lane) and scored against every query head of the KV group
 //    (or, with a shared choice, their sum); the per-lane partial dot products
 //    are summed over the half wave.  Scores go to the workspace, [B, Hq, nblk].
-//  * block_select_kernel: one work-group per (query head, sequence).  Block
-//    scores as (score key, inverted block index) keys, so that one maximum
-//    search orders by score with ties to the lower block; the nsel largest by
-//    repeated wave maxima (per wave, then over the four waves' survivors),
-//    written in ascending block order.
-//  * block_attn_kernel: one work-group per (query head, sequence).  The
-//    visible ranges (sinks, chosen blocks, window) are merged into disjoint
-//    ascending ranges; the four waves take 64-token chunks in turn.  Sixteen
-//    lanes share each key and value row (16 bytes each, four rows per load
-//    instruction), with an online softmax per wave and a final merge.
+//  * block_attn_kernel: one work-group per (query head, sequence).  It first
+//    chooses the head's blocks from its scores: (score key, inverted block
+//    index) keys, so that one maximum search orders by score with ties to the
+//    lower block; the nsel largest by repeated wave maxima (per wave, then
+//    over the four waves' survivors), in ascending block order.  The visible
+//    ranges (sinks, chosen blocks, window) are merged into disjoint ascending
+//    ranges; the four waves take 64-token chunks in turn.  Sixteen lanes share
+//    each key and value row (16 bytes each, four rows per load instruction),
+//    with an online softmax per wave and a final merge.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,15 +47,12 @@ bool block_supported(const BlockArgs& a) {
          a.L / a.blk <= kBlkMaxBlocks;
 }
 
-// workspace: chosen blocks [B, Hq, nsel] int32 | block scores [B, Hq, L / blk] fp32
-static size_t block_chosen_bytes(int B, int Hq, int nsel) {
-  return ((size_t)B * Hq * nsel * sizeof(int32_t) + 255) & ~(size_t)255;
-}
+// workspace: block scores [B, Hq, L / blk] fp32
 size_t block_workspace_bytes(int B, int Hq, int L, int nsel, int Hkv, int d, int blk) {
   (void)Hkv;
   (void)d;
   if (blk < 1 || B < 0 || Hq < 1 || nsel < 1 || L < 0) return 0;
-  return block_chosen_bytes(B, Hq, nsel) + (size_t)B * Hq * (L / blk) * sizeof(float);
+  return (size_t)B * Hq * (L / blk) * sizeof(float);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,7 +180,6 @@ __global__ __launch_bounds__(256) void block_score_kernel(BlockScoreArgs a) {
 struct BlockSelArgs {
   const float* scores;  // [B, Hq, nblk]
   int Hq, nblk, nsel;
-  int32_t* chosen;      // [B, Hq, nsel] (workspace)
   int32_t* blocks_out;  // [B, Hq, nsel] or null
 };
 
@@ -222,24 +217,25 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 constexpr int kSelMaxPerLane = kBlkMaxBlocks / 256;  // blocks per thread, at most
 
-// One work-group per (query head, sequence).  Keys (score key << 32 | ~block)
+// The nsel highest blocks of (sequence b, query head h), run by a 256-thread
+// work-group at the start of the attention.  Keys (score key << 32 | ~block)
 // order blocks by score, ties to the lower block, so the selection is a
 // plain maximum search: each wave takes the nsel largest keys of its share
 // (nsel rounds of a wave maximum, the winner's lane retiring it), one wave
-// then takes the nsel largest of the 4 nsel survivors the same way.
+// then takes the nsel largest of the 4 nsel survivors the same way.  The
+// chosen blocks land in chs[0, nsel) in ascending order, -1 padded (and in
+// blocks_out when given); the function ends with a barrier.
 template <int KPL>  // keys per thread: blocks n = tid + 256 r, r < KPL
-__global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
-  __shared__ uint64_t cand[4][kBlkMaxSel];
-  __shared__ int pick[kBlkMaxSel];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+__device__ __forceinline__ void block_choose(const BlockSelArgs& a, int b, int h, int* chs,
+                                             uint64_t (*cand)[kBlkMaxSel], int* pick) {
+  const int tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6;
   const int nblk = a.nblk;
   const float* srow = a.scores + ((int64_t)b * a.Hq + h) * nblk;
-  // block n = tid + 256 r
   // All loads are issued before any is used (clamped addresses, masked keys).
   float sv[KPL];
 #pragma unroll
-  for (int r = 0; r < KPL; ++r) sv[r] = srow[min(tid + 256 * r, nblk - 1)];
+  for (int r = 0; r < KPL; ++r) sv[r] = nblk > 0 ? srow[min(tid + 256 * r, nblk - 1)] : 0.f;
   uint64_t key[KPL];
 #pragma unroll
   for (int r = 0; r < KPL; ++r) {
@@ -280,7 +276,6 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
   }
   __syncthreads();
   // ascending order: rank of each chosen block among the chosen (m <= 64)
-  int32_t* ch = a.chosen + ((int64_t)b * a.Hq + h) * a.nsel;
   int32_t* bo = a.blocks_out ? a.blocks_out + ((int64_t)b * a.Hq + h) * a.nsel : nullptr;
   if (tid < a.nsel) {
     int val = -1, rank = tid;
@@ -290,9 +285,10 @@ __global__ __launch_bounds__(256) void block_select_kernel(BlockSelArgs a) {
       for (int i = 0; i < m; ++i) rank += pick[i] < mine;
       val = mine;
     }
-    ch[rank] = val;
+    chs[rank] = val;
     if (bo) bo[rank] = val;
   }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -302,7 +298,7 @@ struct BlockAttnArgs {
   const uint16_t* q;  // [B, Hq, d]
   const uint16_t* k;  // [B, L, Hkv, d]
   const uint16_t* v;
-  const int32_t* chosen;  // [B, Hq, nsel], ascending, -1 padded
+  BlockSelArgs sel;   // the block scores, and where the choice is reported
   int B, L, Hq, Hkv, blk, nsel, n_sink, n_win;
   float scale_log2;
   float* out;  // [B, Hq, d]
@@ -318,7 +314,10 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+template <int KPL>
 __global__ __launch_bounds__(256) void block_attn_kernel(BlockAttnArgs a) {
+  __shared__ uint64_t cand[4][kBlkMaxSel];
+  __shared__ int pick[kBlkMaxSel];
   __shared__ int rs[kBlkMaxRanges], re[kBlkMaxRanges], rcum[kBlkMaxRanges + 1];
   __shared__ int st[kBlkMaxRanges], en[kBlkMaxRanges];  // unsorted ranges
   __shared__ int s_nr;
@@ -338,9 +337,9 @@ __global__ __launch_bounds__(256) void block_attn_kernel(BlockAttnArgs a) {
   const int g = h / (a.Hq / a.Hkv);
   const int L = a.L;
 
-  // ---- visible ranges: sinks, chosen blocks, window -> disjoint, ascending
-  if (tid < a.nsel) chs[tid] = a.chosen[((int64_t)b * a.Hq + h) * a.nsel + tid];
-  __syncthreads();
+  // ---- the chosen blocks, then the visible ranges: sinks, chosen blocks,
+  // window -> disjoint, ascending
+  block_choose<KPL>(a.sel, b, h, chs, cand, pick);
   if (tid == 0) {
     int n = 0;
     if (a.n_sink > 0) {
@@ -521,7 +520,7 @@ hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d, int bl
 hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int nblk = a.L / a.blk;
-  float* scores = (float*)((char*)a.ws + block_chosen_bytes(a.B, a.Hq, a.nsel));
+  float* scores = (float*)a.ws;
   if (nblk > 0) {
     BlockScoreArgs c{};
     c.q = (const uint16_t*)a.q;
@@ -542,29 +541,15 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  BlockSelArgs s{};
-  s.scores = scores;
-  s.Hq = a.Hq;
-  s.nblk = nblk;
-  s.nsel = a.nsel;
-  s.chosen = (int32_t*)a.ws;
-  s.blocks_out = a.blocks_out;
-  const dim3 sgrid((unsigned)a.Hq, (unsigned)a.B);
-  if (nblk <= 256 * 4)
-    block_select_kernel<4><<<sgrid, 256, 0, st>>>(s);
-  else if (nblk <= 256 * 8)
-    block_select_kernel<8><<<sgrid, 256, 0, st>>>(s);
-  else if (nblk <= 256 * 16)
-    block_select_kernel<16><<<sgrid, 256, 0, st>>>(s);
-  else
-    block_select_kernel<kSelMaxPerLane><<<sgrid, 256, 0, st>>>(s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   BlockAttnArgs t{};
+  t.sel.scores = scores;
+  t.sel.Hq = a.Hq;
+  t.sel.nblk = nblk;
+  t.sel.nsel = a.nsel;
+  t.sel.blocks_out = a.blocks_out;
   t.q = (const uint16_t*)a.q;
   t.k = (const uint16_t*)a.k;
   t.v = (const uint16_t*)a.v;
-  t.chosen = s.chosen;
   t.B = a.B;
   t.L = a.L;
   t.Hq = a.Hq;
@@ -575,7 +560,15 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   t.n_win = a.n_win;
   t.scale_log2 = a.sm_scale * kLog2e;
   t.out = a.out;
-  block_attn_kernel<<<dim3((unsigned)(a.Hq * a.B)), 256, 0, st>>>(t);
+  const dim3 grid((unsigned)(a.Hq * a.B));
+  if (nblk <= 256 * 4)
+    block_attn_kernel<4><<<grid, 256, 0, st>>>(t);
+  else if (nblk <= 256 * 8)
+    block_attn_kernel<8><<<grid, 256, 0, st>>>(t);
+  else if (nblk <= 256 * 16)
+    block_attn_kernel<16><<<grid, 256, 0, st>>>(t);
+  else
+    block_attn_kernel<kSelMaxPerLane><<<grid, 256, 0, st>>>(t);
   return hipGetLastError();
 }
 
