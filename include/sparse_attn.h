@@ -287,7 +287,8 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w,
  *
  * sparse_attn_block_pool: krep[b, n, g, :] = mean over the blk tokens of block
  * n of k[b, :, g, :], for the complete blocks n < L / blk.
- *   k [B, L, Hkv, d] bf16; krep [B, L/blk, Hkv, d] fp32 output.
+ *   k [B, L, Hkv, d] bf16; krep [B, L/blk, Hkv, d] fp32 output (may be NULL
+ *   when L < blk: there is no complete block).
  *
  * sparse_attn_block_decode: per query head h (KV head g = h / (Hq / Hkv)):
  *   block score n = q[b,h,:] . krep[b,n,g,:]; the nsel highest (ties to the
@@ -298,7 +299,8 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w,
  *   ranked by the sum of the group's block scores, ties to the lower block
  *   ("MLA 与稀疏注意力" section on choosing blocks and merging outputs, and its
  *   worked example); 0: each query head chooses by its own scores.
- *   q [B, Hq, d] bf16; k, v [B, L, Hkv, d] bf16; krep from block_pool.
+ *   q [B, Hq, d] bf16; k, v [B, L, Hkv, d] bf16; krep from block_pool (may
+ *   be NULL when L < blk: then only sinks and window are visible).
  *   out [B, Hq, d] fp32; blocks_out [B, Hq, nsel] int32 (may be NULL): the
  *   selected block indices in ascending order (-1 when fewer blocks exist).
  * Compiled set: d = 128, blk in {32, 64, 128}, Hq / Hkv in {1, 2, 4, 8},

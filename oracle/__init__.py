@@ -50,7 +50,7 @@ def lib():
                                      I, D, P, P]
         L.orc_block_pool.argtypes = [P, I, I, I, I, I, P]
         L.orc_block_sparse_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I,
-                                              I, I, D, I, P, P]
+                                              I, I, D, I, P, P, P]
         for f in ("orc_indexer", "orc_topk", "orc_sparse_mla", "orc_masked_mla",
                   "orc_block_pool", "orc_block_sparse_decode"):
             getattr(L, f).restype = I
@@ -276,20 +276,29 @@ def block_pool(k, blk):
 
 
 def block_sparse_decode(q, k, v, blk, nsel, n_sink, n_win, sm_scale, krep=None,
-                        shared=False):
+                        shared=False, given_blocks=None, allow_empty=False):
     """GQA block-sparse decode -> (out[B,Hq,d], blocks[B,Hq,nsel]).
 
     shared=True: the query heads of a KV group share one block choice, by the
-    sum of their block scores ("MLA 与稀疏注意力", block choice and merging)."""
+    sum of their block scores ("MLA 与稀疏注意力", block choice and merging).
+    given_blocks[B,Hq,nsel]: attend over these blocks (entries outside
+    [0, L // blk) ignored) instead of choosing; blocks then echoes the given
+    valid blocks in ascending order.  allow_empty: a head with an empty
+    visible set gets out = 0 instead of raising."""
     qd, kd, vd = decode(q), decode(k), decode(v)
     B, Hq, d = qd.shape
     L, Hkv = kd.shape[1], kd.shape[2]
     kr = block_pool(k, blk) if krep is None else decode(krep)
     out = np.empty((B, Hq, d), dtype=np.float64)
     blocks = np.empty((B, Hq, max(nsel, 1)), dtype=np.int32)
-    _check(lib().orc_block_sparse_decode(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(kr),
+    gb = None
+    if given_blocks is not None:
+        gb = _i32(given_blocks)
+        assert gb.shape == (B, Hq, nsel), "given_blocks must be [B, Hq, nsel]"
+    code = lib().orc_block_sparse_decode(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(kr),
                                          B, L, Hq, Hkv, d, blk, nsel, n_sink,
                                          n_win, sm_scale, int(bool(shared)),
-                                         _ptr(out), _ptr(blocks)),
-           "block_sparse_decode")
+                                         _ptr(gb), _ptr(out), _ptr(blocks))
+    if not (allow_empty and code == ERR_EMPTY):
+        _check(code, "block_sparse_decode")
     return out, blocks[..., :nsel]

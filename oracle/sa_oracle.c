@@ -342,7 +342,8 @@ int orc_block_pool(const double* k, int B, int L, int Hkv, int d, int blk,
 int orc_block_sparse_decode(const double* q, const double* k, const double* v,
                             const double* krep, int B, int L, int Hq, int Hkv,
                             int d, int blk, int nsel, int n_sink, int n_win,
-                            double sm_scale, int shared, double* out,
+                            double sm_scale, int shared,
+                            const int32_t* given_blocks, double* out,
                             int32_t* blocks_out) {
   if (!q || !k || !v || !krep || !out || B < 0 || L < 1 || Hq < 1 ||
       Hkv < 1 || Hq % Hkv || d < 1 || blk < 1 || nsel < 0 || n_sink < 0 ||
@@ -368,9 +369,10 @@ int orc_block_sparse_decode(const double* q, const double* k, const double* v,
       int b = (int)(u / Hq), h = (int)(u % Hq), g = h / group;
       const double* qh = q + u * d;
       /* block scores against the mean-pooled block keys: the head's own, or
-         with `shared` the sum over the heads of its KV group */
+         with `shared` the sum over the heads of its KV group; a given choice
+         replaces the scoring and the ranking */
       int h0 = shared ? g * group : h, h1 = shared ? h0 + group : h + 1;
-      for (int n = 0; n < nblk; ++n) {
+      for (int n = 0; n < nblk && !given_blocks; ++n) {
         const double* kr = krep + (((int64_t)b * nblk + n) * Hkv + g) * d;
         double total = 0.0;
         for (int hh = h0; hh < h1; ++hh) {
@@ -382,9 +384,17 @@ int orc_block_sparse_decode(const double* q, const double* k, const double* v,
         c[n].score = total;
         c[n].pos = n;
       }
-      qsort(c, (size_t)nblk, sizeof(cand_t), by_neg_score_then_pos);
-      int m = nblk < nsel ? nblk : nsel;
-      for (int i = 0; i < m; ++i) sel[i] = c[i].pos;
+      int m = 0;
+      if (given_blocks) {
+        for (int i = 0; i < nsel; ++i) {
+          int32_t x = given_blocks[u * nsel + i];
+          if (x >= 0 && x < nblk) sel[m++] = x;
+        }
+      } else {
+        qsort(c, (size_t)nblk, sizeof(cand_t), by_neg_score_then_pos);
+        m = nblk < nsel ? nblk : nsel;
+        for (int i = 0; i < m; ++i) sel[i] = c[i].pos;
+      }
       qsort(sel, (size_t)m, sizeof(int32_t), by_pos);
       if (blocks_out)
         for (int i = 0; i < nsel; ++i)

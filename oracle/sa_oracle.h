@@ -109,13 +109,20 @@ int orc_masked_mla(const double* q_lat, const double* q_rope,
  *   in ascending order.
  *   shared != 0: the block choice is shared by the query heads of a KV group,
  *   by the sum of their block scores, ties to the lower block index
- *   ["MLA 与稀疏注意力" section on block choice and merging, worked example]. */
+ *   ["MLA 与稀疏注意力" section on block choice and merging, worked example].
+ *   given_blocks[B, Hq, nsel] (may be NULL): when given, no block is chosen;
+ *   the visible set is built from these block indices instead (entries
+ *   outside [0, L / blk) are ignored, a block listed twice counts once), so a
+ *   caller can evaluate the attention of a choice made elsewhere.  With the
+ *   oracle's own choice passed in, the output is the same as without.
+ *   Returns ORC_ERR_EMPTY (out = 0) when some head's visible set is empty. */
 int orc_block_pool(const double* k, int B, int L, int Hkv, int d, int blk,
                    double* krep);
 int orc_block_sparse_decode(const double* q, const double* k, const double* v,
                             const double* krep, int B, int L, int Hq, int Hkv,
                             int d, int blk, int nsel, int n_sink, int n_win,
-                            double sm_scale, int shared, double* out,
+                            double sm_scale, int shared,
+                            const int32_t* given_blocks, double* out,
                             int32_t* blocks_out);
 
 #ifdef __cplusplus

@@ -135,13 +135,19 @@ def test_block_validation(lib):
     assert f(A, A, A, A, 1, 4096, 6, 2, 128, 64, 16, 64, 512, F, 0, A, None, A, 1 << 20, None) == 5
     # shared_choice is a flag
     assert f(A, A, A, A, 1, 4096, 8, 2, 128, 64, 16, 64, 512, F, 2, A, None, A, 1 << 20, None) == 2
-    # workspace too small: the chosen blocks [B, Hq, nsel]
+    # workspace too small: the block scores [B, Hq, L / blk]
     need = lib.sparse_attn_workspace_bytes(3, 1, 8, 4096, 16, 2, 128)
     assert need >= 8 * 16 * 4
     assert f(A, A, A, A, 1, 4096, 8, 2, 128, 64, 16, 64, 512, F, 0, A, None, A, 16, None) == 6
     pool = lib.sparse_attn_block_pool
     assert pool(A, 1, 4096, 2, 128, 48, A, None) == 5  # block size not compiled
     assert pool(None, 1, 4096, 2, 128, 64, A, None) == 1
+    assert pool(A, 1, 4096, 2, 128, 64, None, None) == 1
+    # no complete block (L < blk): krep may be NULL, and nothing is enqueued
+    assert pool(A, 1, 40, 2, 128, 64, None, None) == 0
+    # the decode still needs krep when blocks exist
+    assert f(A, A, A, None, 1, 4096, 8, 2, 128, 64, 16, 64, 512, F, 0, A, None, A, 1 << 20,
+             None) == 1
 
 
 def test_prefill_select_validation(lib):

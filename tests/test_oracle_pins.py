@@ -535,6 +535,55 @@ def test_block_sparse_all_blocks_is_dense(orc):
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_block_sparse_given_blocks_reproduces_own_choice(orc):
+    # passing the oracle's own choice back in gives the same output, bit for
+    # bit, and echoes the same blocks (per head and with a shared choice)
+    g = torch.Generator().manual_seed(18)
+    B, L, Hq, Hkv, d, blk = 2, 100, 4, 2, 8, 8
+    q = torch.randn(B, Hq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, L, Hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, L, Hkv, d, generator=g, dtype=torch.float64)
+    for shared in (False, True):
+        out, blocks = orc.block_sparse_decode(q, k, v, blk, 3, 2, 7, 0.35, shared=shared)
+        o2, b2 = orc.block_sparse_decode(q, k, v, blk, 3, 2, 7, 0.35, given_blocks=blocks)
+        np.testing.assert_array_equal(b2, blocks)
+        np.testing.assert_array_equal(o2, out)
+
+
+def test_block_sparse_given_blocks_is_masked_softmax(orc):
+    # an arbitrary given choice (not the top blocks; with a duplicate, an
+    # out-of-range entry and -1 padding) attends over exactly the union of
+    # those blocks, the sinks and the window: torch SDPA with that mask
+    g = torch.Generator().manual_seed(19)
+    B, L, Hq, Hkv, d, blk = 1, 70, 2, 1, 8, 8   # 8 complete blocks, ragged tail
+    q = torch.randn(B, Hq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, L, Hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, L, Hkv, d, generator=g, dtype=torch.float64)
+    given = np.array([[[5, 1, 5, -1], [8, 0, 3, 7]]], dtype=np.int32)  # 8 is past the blocks
+    out, blocks = orc.block_sparse_decode(q, k, v, blk, 4, 2, 3, 0.5, given_blocks=given)
+    assert blocks[0, 0].tolist()[:2] == [1, 5] and blocks[0, 1].tolist()[:3] == [0, 3, 7]
+    mask = torch.zeros(Hq, L, dtype=torch.bool)
+    for h, bl in ((0, [1, 5]), (1, [0, 3, 7])):
+        for bi in bl:
+            mask[h, bi * blk:(bi + 1) * blk] = True
+    mask[:, :2] = True
+    mask[:, L - 3:] = True
+    ref = _sdpa_masked(q[0], k[0], v[0], mask, 0.5)
+    np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_block_sparse_empty_visible_set(orc):
+    # L < blk, no sinks, no window: nothing is visible; out = 0 when allowed
+    g = torch.Generator().manual_seed(20)
+    q = torch.randn(1, 2, 4, generator=g, dtype=torch.float64)
+    k = torch.randn(1, 5, 1, 4, generator=g, dtype=torch.float64)
+    v = torch.randn(1, 5, 1, 4, generator=g, dtype=torch.float64)
+    with pytest.raises(orc.OracleError):
+        orc.block_sparse_decode(q, k, v, 8, 2, 0, 0, 0.5)
+    out, blocks = orc.block_sparse_decode(q, k, v, 8, 2, 0, 0, 0.5, allow_empty=True)
+    assert np.all(out == 0) and np.all(blocks == -1)
+
+
 # --------------------------------------------------------------------------
 # GQA-shared block choice (the group's heads share one block set)
 # --------------------------------------------------------------------------

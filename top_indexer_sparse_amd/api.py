@@ -379,7 +379,8 @@ def sparse_attn_block_pool(k, blk, krep=None, stream=None):
     if krep is None:
         krep = torch.empty((B, L // blk, Hkv, d), dtype=torch.float32, device=k.device)
     _need(krep, "krep", (torch.float32,), (B, L // blk, Hkv, d))
-    _call("sparse_attn_block_pool", _ptr(k), B, L, Hkv, d, blk, _ptr(krep), _stream(stream))
+    _call("sparse_attn_block_pool", _ptr(k), B, L, Hkv, d, blk, _ptr(krep) if krep.numel() else None,
+          _stream(stream))
     return krep
 
 
@@ -402,7 +403,8 @@ def sparse_attn_block_decode(q, k, v, krep, blk, nsel, n_sink, n_win, sm_scale, 
     _need(blocks_out, "blocks_out", (torch.int32,), (B, Hq, nsel))
     ws, nb = _workspace(ws, sparse_attn_workspace_bytes(SA_OP_BLOCK_DECODE, B, Hq, L, nsel, Hkv,
                                                         d), dev)
-    _call("sparse_attn_block_decode", _ptr(q), _ptr(k), _ptr(v), _ptr(krep), B, L, Hq, Hkv, d,
+    _call("sparse_attn_block_decode", _ptr(q), _ptr(k), _ptr(v),
+          _ptr(krep) if krep.numel() else None, B, L, Hq, Hkv, d,
           blk, nsel, n_sink, n_win, float(sm_scale), int(bool(shared_choice)), _ptr(out),
           _ptr(blocks_out), _ptr(ws), nb, _stream(stream))
     return out, blocks_out

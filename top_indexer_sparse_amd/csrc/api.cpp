@@ -376,8 +376,9 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w, c
 int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, float* krep,
                            void* stream) {
   clear_error();
-  REQUIRE(k && krep, SA_ERR_NULL, "block_pool: k and krep are required");
   REQUIRE(B >= 0 && L >= 0 && Hkv >= 1 && blk >= 1, SA_ERR_SHAPE, "block_pool: bad size");
+  // krep holds L / blk blocks: with no complete block it may be NULL
+  REQUIRE(k && (krep || L / blk == 0), SA_ERR_NULL, "block_pool: k and krep are required");
   REQUIRE(d == 128, SA_ERR_UNSUPPORTED, "block_pool: d=%d not 128", d);
   REQUIRE(blk == 32 || blk == 64 || blk == 128, SA_ERR_UNSUPPORTED, "block_pool: blk=%d not in {32,64,128}", blk);
   REQUIRE(aligned16(k) && aligned16(krep), SA_ERR_ALIGN, "block_pool: pointers must be 16-byte aligned");
@@ -393,9 +394,11 @@ int sparse_attn_block_decode(const void* q, const void* k, const void* v, const 
                   shared_choice, out, blocks_out, ws};
   REQUIRE(shared_choice == 0 || shared_choice == 1, SA_ERR_SHAPE,
           "block_decode: shared_choice must be 0 or 1");
-  REQUIRE(q && k && v && krep && out, SA_ERR_NULL, "block_decode: q, k, v, krep and out are required");
   REQUIRE(B >= 0 && L >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && n_sink >= 0 && n_win >= 0 && nsel >= 1,
           SA_ERR_SHAPE, "block_decode: bad size");
+  // with no complete block (L < blk) krep holds nothing and may be NULL
+  REQUIRE(q && k && v && out && (krep || L / blk == 0), SA_ERR_NULL,
+          "block_decode: q, k, v, krep and out are required");
   REQUIRE(sa::block_supported(a), SA_ERR_UNSUPPORTED, "block_decode: dims outside the compiled set");
   REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(krep) && aligned16(out) &&
               aligned16(blocks_out) && aligned16(ws),
