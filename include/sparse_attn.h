@@ -189,6 +189,30 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w,
                        void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sparse_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The scratch is a fixed 64 MiB array
+ * inside the library, one per GPU, held until the process ends; this call
+ * allocates nothing and calls no allocating routine.  Arguments, outputs and
+ * errors as sparse_attn_decode; sizes whose workspace
+ * (sparse_attn_workspace_bytes(SA_OP_DECODE, ...)) exceeds 64 MiB return
+ * SA_ERR_WORKSPACE before anything is enqueued.  The scratch is shared by
+ * every call on the same GPU: calls that overlap in time on one GPU (other
+ * streams or threads) race on it, so callers serialise them.  It needs no
+ * clearing: every part of it is written before it is read.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_decode_noalloc(const void* q_idx, int q_idx_dtype,
+                               const float* w, const void* k_idx, int k_dtype,
+                               const float* k_scale, const int32_t* kv_len,
+                               int B, int L, int HI, int dI, int k,
+                               const void* q_lat, const void* q_rope,
+                               int q_dtype, const void* c_kv,
+                               const void* k_rope, int kv_dtype,
+                               int64_t c_stride, int64_t r_stride, int H,
+                               int dc, int dR, float sm_scale, float* out,
+                               float* lse, int32_t* idx_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Fused prefill select: stages 1 and 2 in one kernel, with no [B, T, L] score
  * tensor.  "MLA 与稀疏注意力" DSA section (I_{t,s}, then TopK over s <= t);
  * "Sparse Attention 数学学习笔记" §9.  One work-group per query row computes

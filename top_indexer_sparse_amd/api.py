@@ -26,7 +26,8 @@ _DTYPE = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: S
 
 EXPORTS = (
     "sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
-    "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode",
+    "sparse_attn_decode", "sparse_attn_decode_noalloc", "sparse_attn_block_pool",
+    "sparse_attn_block_decode",
     "sparse_attn_csa_decode", "sparse_attn_prefill_select", "sparse_attn_prefill",
     "sparse_attn_workspace_bytes", "sparse_attn_status_string", "sparse_attn_last_error",
 )
@@ -60,6 +61,8 @@ def load():
                                           I, F, P, P, P, SZ, P]
     L.sparse_attn_decode.argtypes = [P, I, P, P, I, P, P, I, I, I, I, I, P, P, I, P, P, I,
                                      I64, I64, I, I, I, F, P, P, P, P, SZ, P]
+    L.sparse_attn_decode_noalloc.argtypes = [P, I, P, P, I, P, P, I, I, I, I, I, P, P, I, P, P,
+                                             I, I64, I64, I, I, I, F, P, P, P, P]
     L.sparse_attn_block_pool.argtypes = [P, I, I, I, I, I, P, P]
     L.sparse_attn_block_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
                                            P, P, SZ, P]
@@ -75,8 +78,8 @@ def load():
     L.sparse_attn_last_error.argtypes = []
     L.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_indexer_scores", "sparse_attn_topk", "sparse_attn_mla_forward",
-              "sparse_attn_decode", "sparse_attn_block_pool", "sparse_attn_block_decode",
-              "sparse_attn_csa_decode", "sparse_attn_prefill_select", "sparse_attn_prefill"):
+              "sparse_attn_decode", "sparse_attn_decode_noalloc", "sparse_attn_block_pool",
+              "sparse_attn_block_decode", "sparse_attn_csa_decode", "sparse_attn_prefill_select", "sparse_attn_prefill"):
         getattr(L, f).restype = I
     _lib = L
     return L
@@ -224,9 +227,9 @@ def sparse_attn_mla_forward(q_lat, q_rope, c_kv, k_rope, idx, sm_scale, out=None
     return out, lse
 
 
-def sparse_attn_decode(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_kv, k_rope,
-                       sm_scale, out=None, lse=None, idx_out=None, ws=None, stream=None):
-    """Fused decode step (T = 1) -> (out [B,1,H,dc], lse [B,1,H], idx [B,1,k])."""
+def _decode_args(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_kv, k_rope, sm_scale,
+                 out, lse, idx_out):
+    """Checked arguments of the fused decode, up to the workspace."""
     B, T, HI, dI = q_idx.shape
     if T != 1:
         raise ValueError("sparse_attn_decode takes one query per sequence (T = 1)")
@@ -254,11 +257,32 @@ def sparse_attn_decode(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_
     _need(out, "out", (torch.float32,), (B, 1, H, dc))
     _need(lse, "lse", (torch.float32,), (B, 1, H))
     _need(idx_out, "idx_out", (torch.int32,), (B, 1, topk))
+    args = (_ptr(q_idx), _DTYPE[q_idx.dtype], _ptr(w), _ptr(k_idx), _DTYPE[k_idx.dtype],
+            _ptr(k_scale), _ptr(kv_len), B, L, HI, dI, topk, _ptr(q_lat), _ptr(q_rope), _DTYPE[dt],
+            _ptr(c_kv), _ptr(k_rope), _DTYPE[dt], cs, rs, H, dc, dR, float(sm_scale), _ptr(out),
+            _ptr(lse), _ptr(idx_out))
+    return args, out, lse, idx_out, (B, L, H, dc, dev)
+
+
+def sparse_attn_decode(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_kv, k_rope,
+                       sm_scale, out=None, lse=None, idx_out=None, ws=None, stream=None):
+    """Fused decode step (T = 1) -> (out [B,1,H,dc], lse [B,1,H], idx [B,1,k])."""
+    args, out, lse, idx_out, (B, L, H, dc, dev) = _decode_args(
+        q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_kv, k_rope, sm_scale, out, lse,
+        idx_out)
     ws, nb = _workspace(ws, sparse_attn_workspace_bytes(SA_OP_DECODE, B, 1, L, topk, H, dc), dev)
-    _call("sparse_attn_decode", _ptr(q_idx), _DTYPE[q_idx.dtype], _ptr(w), _ptr(k_idx),
-          _DTYPE[k_idx.dtype], _ptr(k_scale), _ptr(kv_len), B, L, HI, dI, topk, _ptr(q_lat),
-          _ptr(q_rope), _DTYPE[dt], _ptr(c_kv), _ptr(k_rope), _DTYPE[dt], cs, rs, H, dc, dR,
-          float(sm_scale), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), nb, _stream(stream))
+    _call("sparse_attn_decode", *args, _ptr(ws), nb, _stream(stream))
+    return out, lse, idx_out
+
+
+def sparse_attn_decode_noalloc(q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_kv,
+                               k_rope, sm_scale, out=None, lse=None, idx_out=None, stream=None):
+    """sparse_attn_decode with the library's fixed per-GPU scratch instead of a
+    workspace; with out, lse and idx_out given, nothing is allocated."""
+    args, out, lse, idx_out, _ = _decode_args(
+        q_idx, w, k_idx, k_scale, kv_len, topk, q_lat, q_rope, c_kv, k_rope, sm_scale, out, lse,
+        idx_out)
+    _call("sparse_attn_decode_noalloc", *args, _stream(stream))
     return out, lse, idx_out
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "sparse_attn.h"
@@ -171,6 +172,36 @@ int check_prefill_select(const sa::IndexerArgs& a, int k, bool allow_long = fals
   return SA_OK;
 }
 
+// Scratch of sparse_attn_decode_noalloc: one array per GPU the library runs
+// on, held until the process ends.  Host code never uses the array's name as
+// an address (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device,
+// and is kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (resolved on first use).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA_ERR_UNSUPPORTED, "decode_noalloc: device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "decode_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,6 +271,28 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w, const
   if (s == SA_OK) s = hip_status(sa::launch_topk(ta, st), "decode topk launch");
   if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "decode mla launch");
   return s;
+}
+
+int sparse_attn_decode_noalloc(const void* q_idx, int q_idx_dtype, const float* w, const void* k_idx,
+                               int k_dtype, const float* k_scale, const int32_t* kv_len, int B, int L,
+                               int HI, int dI, int k, const void* q_lat, const void* q_rope,
+                               int q_dtype, const void* c_kv, const void* k_rope, int kv_dtype,
+                               int64_t c_stride, int64_t r_stride, int H, int dc, int dR,
+                               float sm_scale, float* out, float* lse, int32_t* idx_out,
+                               void* stream) {
+  clear_error();
+  REQUIRE(B >= 0 && L >= 0, SA_ERR_SHAPE, "decode_noalloc: negative size B=%d L=%d", B, L);
+  const size_t need = decode_ws(B, L, k < 1 ? 1 : k, H, dc, kv_dtype).total;
+  REQUIRE(need <= kScratchBytes, SA_ERR_WORKSPACE,
+          "decode_noalloc: these sizes need %zu bytes of scratch, above the library's fixed %zu "
+          "(use sparse_attn_decode with a workspace)",
+          need, kScratchBytes);
+  void* ws = nullptr;
+  int s = scratch_address(&ws);
+  if (s != SA_OK) return s;
+  return sparse_attn_decode(q_idx, q_idx_dtype, w, k_idx, k_dtype, k_scale, kv_len, B, L, HI, dI, k,
+                            q_lat, q_rope, q_dtype, c_kv, k_rope, kv_dtype, c_stride, r_stride, H, dc,
+                            dR, sm_scale, out, lse, idx_out, ws, kScratchBytes, stream);
 }
 
 int sparse_attn_prefill_select(const void* q_idx, int q_dtype, const float* w, const void* k_idx,
