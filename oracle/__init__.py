@@ -16,7 +16,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SA_ORACLE_LIB selects another build of the same source (the sanitizer build)
+_LIB_PATH = os.environ.get("SA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 OK, ERR_ARG, ERR_NONFINITE, ERR_EMPTY, ERR_NOMEM = 0, -1, -2, -3, -4

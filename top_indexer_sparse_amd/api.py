@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+# SA_LIB selects another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("SA_LIB") or os.path.join(_HERE, "libsparse_attn.so")
 
 SA_OK = 0
 SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
