@@ -33,6 +33,13 @@ struct KeyChunk {
       raw[i] = *(const uintx4*)(row + off);
     }
   }
+  // The same 16-byte pieces from a row stored with piece p at p ^ x (an LDS
+  // tile swizzled against bank conflicts; the piece index of load i, lane
+  // group g is 4 i + g for both key types).
+  __device__ __forceinline__ void load_swz(const uint8_t* row, int g, int x) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) raw[i] = *(const uintx4*)(row + 16 * ((4 * i + g) ^ x));
+  }
   __device__ __forceinline__ bf16x8 operand(int ks) const {
     if constexpr (!FP8) {
       return as_bf16x8(raw[ks]);

@@ -195,7 +195,8 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
 }
 
 // Eight waves = eight consecutive queries of one sequence; 64-position key
-// tiles staged in LDS (rows padded by 16 bytes against bank conflicts).
+// tiles staged in LDS (each row's 16-byte pieces swizzled by the row index,
+// so the waves' operand reads and the staging stores avoid bank conflicts).
 constexpr int kPfWaves = 8;
 constexpr int kPfTile = 64;
 
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(HT <= 4 ? 4
     int T, int L, float* __restrict__ scores) {
   constexpr int HI = 16 * HT;
   constexpr int ROWB = FP8 ? DI : 2 * DI;
-  constexpr int LROW = ROWB + 16;                 // padded LDS row
+  constexpr int LROW = ROWB;                      // LDS row: pieces swizzled, not padded
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
   constexpr int CPT = kPfTile * CPR;              // chunks per tile
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPfTile * LROW];
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(HT <= 4 ? 4
       const int c = threadIdx.x + 512 * i;
       if (c < CPT) {
         const int r = c / CPR, o = c % CPR;
-        *(uintx4*)(&tile[buf][r * LROW + 16 * o]) = stage[i];
+        *(uintx4*)(&tile[buf][r * LROW + 16 * (o ^ (r & (CPR - 1)))]) = stage[i];
       }
     }
     if (scb && threadIdx.x < kPfTile)
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(HT <= 4 ? 4
         const int s0 = base + 16 * c;
         if (s0 >= lim) break;
         KeyChunk<DI, FP8> kc;
-        kc.load(&tile[buf][(16 * c + n) * LROW], g);
+        kc.load_swz(&tile[buf][(16 * c + n) * LROW], g, n & (CPR - 1));
         float sc = qr.score(kc);
         const int s = s0 + n;
         if (g == 0 && s < lim) {

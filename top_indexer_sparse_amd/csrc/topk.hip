@@ -40,6 +40,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "select_core.hpp"
+#include "split_select.hpp"
 
 namespace sa {
 
@@ -118,21 +119,6 @@ __device__ __forceinline__ void find_rank_bins(const int* hist, Ranks ranks, int
     found[2] = blo;
   }
   __syncthreads();
-}
-
-// hist[d] += 1 for every lane with `valid`.  When all valid lanes of the wave
-// share one bin, one lane adds the whole count instead of 64 lanes hitting
-// the same LDS word.
-__device__ __forceinline__ void hist_add(int* hist, uint32_t d, bool valid) {
-  const uint64_t m = __ballot(valid);
-  if (m == 0) return;
-  const int lead = __ffsll((unsigned long long)m) - 1;
-  const uint32_t d0 = __builtin_amdgcn_readlane(d, lead);
-  if (__ballot(valid && d == d0) == m) {
-    if (lane_id() == lead) atomicAdd(&hist[d0], __popcll(m));
-  } else if (valid) {
-    atomicAdd(&hist[d], 1);
-  }
 }
 
 struct TopkRowArgs {
@@ -483,7 +469,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
 //     scores instead (radix passes over the whole row), so correctness never
 //     rests on the sample.
 // ---------------------------------------------------------------------------
-constexpr int kSpChunk = 4096;
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpPer = kSpChunk / kSpThreads;  // consecutive positions per thread
@@ -491,10 +476,8 @@ constexpr int kSpRuns = 128, kSpRun = 16;      // the row sample: 2048 keys
 constexpr int kSpSamplePer = kSpRuns * kSpRun / kSpThreads;
 constexpr int kSpRunThreads = kSpThreads / kSpRuns;  // threads per sample run
 static_assert(kSpRunThreads * kSpSamplePer == kSpRun, "a run is split evenly over threads");
-constexpr int kSpBins = 2048;
 constexpr int kSpMaxRows = 128;    // rows of a launch taking the split path
 constexpr int kSpMinL = 8192;      // shortest row length taking it
-constexpr int kSpMaxChunks = 256;  // rows up to 1M positions
 constexpr int kSpKeep = 16384;     // kept keys the second launch holds in LDS
 constexpr int kSpSelThreads = 512; // threads of a select work-group (one per row)
 
@@ -511,76 +494,6 @@ struct TopkSplitArgs {
   int32_t* idx;        // [rows][k]
   int32_t* count;      // [rows] or null
 };
-
-// Exclusive block scan over the NT threads of a split work-group.
-template <int NT = kSpThreads>
-__device__ __forceinline__ int sp_scan_excl(int x, int* red, int& total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int incl = wave_scan_incl(x);
-  __syncthreads();
-  if (lane == 63) red[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int v = red[w];
-    before += w < wave ? v : 0;
-    total += v;
-  }
-  return incl - x + before;
-}
-
-// Bins of `hist` (2048 bins) holding ranks r0 <= r1 counted from the top:
-// found[0] = bin of r0, found[1] = entries in higher bins, found[2] = bin of
-// r1; a rank outside [1, total] gives bin -1.  Thread t owns the BPT =
-// 2048 / NT bins 2047 - BPT t downwards.  Starts with a barrier (the
-// histogram is complete); `found` is visible when it returns.
-template <int NT = kSpThreads>
-__device__ __forceinline__ void sp_rank_bins(const int* hist, int r0, int r1, int* red,
-                                             int* found) {
-  constexpr int BPT = kSpBins / NT;
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    found[0] = found[2] = -1;
-    found[1] = 0;
-  }
-  int h[BPT], own = 0;
-#pragma unroll
-  for (int e = 0; e < BPT; ++e) {
-    h[e] = hist[kSpBins - 1 - BPT * tid - e];
-    own += h[e];
-  }
-  int total;
-  int above = sp_scan_excl<NT>(own, red, total);
-#pragma unroll
-  for (int e = 0; e < BPT; ++e) {
-    if (above < r0 && r0 <= above + h[e]) {
-      found[0] = kSpBins - 1 - BPT * tid - e;
-      found[1] = above;
-    }
-    if (above < r1 && r1 <= above + h[e]) found[2] = kSpBins - 1 - BPT * tid - e;
-    above += h[e];
-  }
-  __syncthreads();
-}
-template <int NT = kSpThreads>
-__device__ __forceinline__ void sp_rank_bin(const int* hist, int r, int* red, int* found) {
-  sp_rank_bins<NT>(hist, r, r, red, found);
-}
-
-template <int NT = kSpThreads>
-__device__ __forceinline__ int sp_block_sum(int x, int* red) {
-  const int t = wave_total(x);
-  __syncthreads();
-  if (lane_id() == 0) red[threadIdx.x >> 6] = t;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) total += red[w];
-  return total;
-}
 
 // Launch A: one work-group per (chunk, row).
 __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitArgs a) {
@@ -670,7 +583,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
     const int r0 = min(max(1, (int)floorf(mean - margin)), ns);
     const int r1u = (int)ceilf(mean + margin);
     const int r1 = min(max(r1u, r0), ns);
-    sp_rank_bins(hist, r0, r1, red, found);
+    sp_rank_bins<kSpThreads>(hist, r0, r1, red, found);
     const int bhi = found[0], blo = found[2];
     hi = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)smin + ((uint64_t)(bhi + 1) << sh) - 1u);
     lo = r1u > ns ? 1u : smin + ((uint32_t)blo << sh);
@@ -687,7 +600,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
     nk += ck[i] != 0u && ck[i] >= lo;
   }
   int tot_packed;
-  int o = sp_scan_excl((na << 16) | nk, red, tot_packed) & 0xffff;
+  int o = sp_scan_excl<kSpThreads>((na << 16) | nk, red, tot_packed) & 0xffff;
   const int64_t base = unit * (int64_t)kSpChunk;
 #pragma unroll
   for (int i = 0; i < kSpPer; ++i) {
@@ -697,7 +610,7 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
       ++o;
     }
   }
-  const int nct = sp_block_sum(nc, red);
+  const int nct = sp_block_sum<kSpThreads>(nc, red);
   if (tid == 0) {
     cnt[0] = tot_packed >> 16;                            // above hi
     cnt[1] = (tot_packed & 0xffff) - (tot_packed >> 16);  // inside [lo, hi]
@@ -708,14 +621,13 @@ __global__ __launch_bounds__(kSpThreads) void topk_split_scan_kernel(TopkSplitAr
   }
 }
 
-// Launch B: one NT-thread work-group per row.
+// Launch B: one NT-thread work-group per row (split_select.hpp).
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) {
-  constexpr int kSelWaves = NT / 64;
   __shared__ uint32_t kk[kSpKeep];
   __shared__ int32_t kp[kSpKeep];
   __shared__ int hist[kSpBins];
-  __shared__ int red[kSelWaves];
+  __shared__ int red[NT / 64];
   __shared__ int found[3];
   __shared__ int preK[kSpMaxChunks + 1];
   __shared__ int tot[4];
@@ -723,197 +635,14 @@ __global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) 
   __shared__ int nsmall;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
-  const int k = a.k;
   const int b = (int)(row / a.T);
   const int lim = candidate_limit(a.q_pos, a.kv_len, b, row, a.L);
-  const int nch = min(a.nchunk, (lim + kSpChunk - 1) / kSpChunk);
-  int32_t* out = a.idx + row * k;
-
-  // ---- the chunks' counts -> offsets of their kept keys ----
-  {
-    const int32_t* cnt = a.cnt + row * a.nchunk * 4;
-    int ca = 0, ci = 0, cc = 0;
-    if (tid < nch) {
-      const int4 c4 = *(const int4*)(cnt + 4 * tid);
-      ca = c4.x;
-      ci = c4.y;
-      cc = c4.z;
-    }
-    int tK;
-    const int ek = sp_scan_excl<NT>(ca + ci, red, tK);
-    const int tA = sp_block_sum<NT>(ca, red);
-    const int tC = sp_block_sum<NT>(cc, red);
-    if (tid < nch) preK[tid] = ek;
-    if (tid == 0) {
-      preK[nch] = tK;
-      tot[0] = tA;
-      tot[1] = tK - tA;
-      tot[2] = tC;
-    }
-    __syncthreads();
-  }
-  const int A = tot[0], I = tot[1], V = tot[2], K = A + I;
-  const int n_sel = min(k, V);
-  const bool fast = V > k && A < k && K >= k && K <= kSpKeep;
-
-  if (fast) {
-    const uint32_t lo = a.bracket[2 * row * a.nchunk], hi = a.bracket[2 * row * a.nchunk + 1];
-    // ---- kept keys into LDS (chunk order = position order): 256 / nch
-    //      threads per chunk, 16 loads in flight per thread and batch ----
-    {
-      const int tpc = NT / nch;  // >= 1
-      const int c = tid / tpc, r = tid % tpc;
-      if (c < nch) {
-        const int n_c = preK[c + 1] - preK[c];
-        const int d0 = preK[c];
-        const int64_t src0 = (row * a.nchunk + c) * (int64_t)kSpChunk;
-        for (int i0 = r; i0 < n_c; i0 += 16 * tpc) {
-          uint32_t vk[16];
-          int32_t vp[16];
-#pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const int i = min(i0 + tpc * m, n_c - 1);
-            vk[m] = a.keepk[src0 + i];
-            vp[m] = a.keepp[src0 + i];
-          }
-#pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const int i = i0 + tpc * m;
-            if (i < n_c) {
-              kk[d0 + i] = vk[m];
-              kp[d0 + i] = vp[m];
-            }
-          }
-        }
-      }
-    }
-    // ---- tau: the (k - A)-th largest inside key, by radix passes over the
-    //      offsets key - lo (11 bits at a time, from the top) ----
-    int krem = k - A;
-    uint32_t prefix = 0u, pmask = 0u;
-    const uint32_t span = hi - lo;
-    int top = span ? 31 - __clz(span) : -1;
-    uint32_t tau = 0u;
-    int need_eq = 0;
-    bool done = false;
-#pragma unroll 1
-    while (top >= 0) {
-      const int width = min(11, top + 1);
-      const int s2 = top + 1 - width;
-      const uint32_t dmask = (1u << width) - 1u;
-      __syncthreads();  // kept keys stored / previous bins read
-      for (int i = tid; i < kSpBins; i += NT) hist[i] = 0;
-      if (tid == 0) nsmall = 0;
-      __syncthreads();
-#pragma unroll 1
-      for (int j0 = 0; j0 < K; j0 += NT) {
-        const int j = j0 + tid;
-        const uint32_t key = j < K ? kk[j] : 0u;
-        const uint32_t c = key - lo;
-        hist_add(hist, (c >> s2) & dmask, j < K && key <= hi && (c & pmask) == prefix);
-      }
-      sp_rank_bin<NT>(hist, krem, red, found);
-      prefix |= (uint32_t)found[0] << s2;
-      pmask |= dmask << s2;
-      krem -= found[1];
-      top = s2 - 1;
-      if (top >= 0 && hist[found[0]] <= 64) {
-        // few keys left in the bin: one wave ranks them directly
-#pragma unroll 1
-        for (int j0 = 0; j0 < K; j0 += NT) {
-          const int j = j0 + tid;
-          const uint32_t key = j < K ? kk[j] : 0u;
-          if (j < K && key <= hi && ((key - lo) & pmask) == prefix) small[atomicAdd(&nsmall, 1)] = key;
-        }
-        __syncthreads();
-        if (tid < 64) {
-          const int n = nsmall;
-          const uint32_t x = tid < n ? small[tid] : 0u;  // kept keys are >= lo >= 1
-          int gt = 0, eq = 0;
-          for (int i = 0; i < n; ++i) {
-            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
-            gt += y > x;
-            eq += y == x;
-          }
-          const uint64_t hit = __ballot(tid < n && gt < krem && krem <= gt + eq);
-          const int lead = __ffsll((unsigned long long)hit) - 1;
-          if (tid == lead) {
-            small[64] = x;
-            small[65] = (uint32_t)(krem - gt);
-          }
-        }
-        __syncthreads();
-        tau = small[64];
-        need_eq = (int)small[65];
-        done = true;
-        break;
-      }
-    }
-    if (!done) {
-      tau = lo + prefix;
-      need_eq = krem;
-    }
-    // ---- ascending output: thread t scans its run of the kept keys ----
-    __syncthreads();
-    const int s = (K + NT - 1) / NT;  // <= 64
-    const int j0 = tid * s, j1 = min(K, j0 + s);
-    int c = 0;
-    for (int j = j0; j < j1; ++j) c += ((kk[j] > tau) << 16) | (kk[j] == tau);
-    int total;
-    const int before = sp_scan_excl<NT>(c, red, total);  // gt, eq <= 16384 each
-    int gtb = before >> 16, eqb = before & 0xffff;
-    for (int j = j0; j < j1; ++j) {
-      const bool g = kk[j] > tau, eq = kk[j] == tau;
-      if (g || (eq && eqb < need_eq)) out[gtb + min(eqb, need_eq)] = kp[j];
-      gtb += g;
-      eqb += eq;
-    }
-  } else {
-    // ---- straight from the row: radix passes over all its keys ----
-    const float* srow = a.scores + row * a.L;
-    uint32_t tau = 0u;  // V <= k: every candidate (key > 0) is taken
-    int need_eq = 0;
-    if (V > k) {
-      int krem = k;
-      uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll 1
-      for (int pass = 0; pass < 3; ++pass) {
-        const int s2 = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-        const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-        __syncthreads();
-        for (int i = tid; i < kSpBins; i += NT) hist[i] = 0;
-        __syncthreads();
-#pragma unroll 1
-        for (int q0 = 0; q0 < lim; q0 += NT) {
-          const int q = q0 + tid;
-          const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
-          hist_add(hist, (c >> s2) & dmask, c != 0u && (c & pmask) == prefix);
-        }
-        sp_rank_bin<NT>(hist, krem, red, found);
-        prefix |= (uint32_t)found[0] << s2;
-        pmask |= dmask << s2;
-        krem -= found[1];
-      }
-      tau = prefix;
-      need_eq = krem;
-    }
-    // emission in position order, 256 positions per round
-    int run_gt = 0, run_eq = 0;
-#pragma unroll 1
-    for (int q0 = 0; q0 < lim; q0 += NT) {
-      const int q = q0 + tid;
-      const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
-      const int g = c != 0u && c > tau, eq = c != 0u && c == tau;
-      int total;
-      const int before = sp_scan_excl<NT>((g << 16) | eq, red, total);
-      const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
-      if (g || (eq && eqb < need_eq)) out[gtb + min(eqb, need_eq)] = q;
-      run_gt += total >> 16;
-      run_eq += total & 0xffff;
-    }
-  }
-  __syncthreads();
-  for (int i = n_sel + tid; i < k; i += NT) out[i] = -1;
+  int32_t* out = a.idx + row * a.k;
+  const SplitView v{a.scores, a.L, a.nchunk, a.cnt, a.bracket, a.keepk, a.keepp};
+  const SplitSmem sm{kk, kp, hist, red, found, preK, tot, small, &nsmall};
+  const int n_sel = split_select<NT, kSpKeep>(
+      v, row, a.k, lim, sm, [&](int slot, int pos) { out[slot] = pos; }, [] {});
+  for (int i = n_sel + tid; i < a.k; i += NT) out[i] = -1;
   if (a.count && tid == 0) a.count[row] = n_sel;
 }
 
@@ -943,26 +672,32 @@ size_t topk_workspace_bytes(int B, int T, int L, int k) {
   return (size_t)rows * nch * k * (sizeof(float) + sizeof(int32_t));
 }
 
+static TopkSplitArgs split_args(const TopkArgs& a) {
+  const int64_t rows = (int64_t)a.B * a.T;
+  TopkSplitArgs sp{};
+  sp.scores = a.scores;
+  sp.q_pos = a.q_pos;
+  sp.kv_len = a.kv_len;
+  sp.T = a.T;
+  sp.L = a.L;
+  sp.k = a.k;
+  sp.nchunk = (a.L + kSpChunk - 1) / kSpChunk;
+  sp.vec4 = (a.L % 4 == 0) && ((uintptr_t)a.scores % 16 == 0);
+  const int64_t units = rows * sp.nchunk;
+  sp.cnt = (int32_t*)a.ws;
+  sp.bracket = (uint32_t*)(sp.cnt + units * 4);
+  sp.keepk = sp.bracket + units * 2;
+  sp.keepp = (int32_t*)(sp.keepk + units * kSpChunk);
+  sp.idx = a.idx;
+  sp.count = a.count;
+  return sp;
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.T;
   if (rows == 0) return hipSuccess;
   if (topk_split(rows, a.L)) {
-    TopkSplitArgs sp{};
-    sp.scores = a.scores;
-    sp.q_pos = a.q_pos;
-    sp.kv_len = a.kv_len;
-    sp.T = a.T;
-    sp.L = a.L;
-    sp.k = a.k;
-    sp.nchunk = (a.L + kSpChunk - 1) / kSpChunk;
-    sp.vec4 = (a.L % 4 == 0) && ((uintptr_t)a.scores % 16 == 0);
-    const int64_t units = rows * sp.nchunk;
-    sp.cnt = (int32_t*)a.ws;
-    sp.bracket = (uint32_t*)(sp.cnt + units * 4);
-    sp.keepk = sp.bracket + units * 2;
-    sp.keepp = (int32_t*)(sp.keepk + units * kSpChunk);
-    sp.idx = a.idx;
-    sp.count = a.count;
+    const TopkSplitArgs sp = split_args(a);
     topk_split_scan_kernel<<<dim3(sp.nchunk, (unsigned)rows), kSpThreads, 0, st>>>(sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
