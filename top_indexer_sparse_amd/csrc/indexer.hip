@@ -10,7 +10,9 @@
 //  * idx_decode_kernel -- bf16 MFMA for few queries (decode).  The query's
 //    HI x dI block stays in registers as the A operand (rows = heads); keys
 //    stream from HBM straight into B-operand registers (columns = positions),
-//    16 positions per step through a 4-deep register ring.  The ReLU * w reduction over
+//    16 positions per step through a register ring of 8 chunks (4 for the
+//    largest query blocks); a query's chunks are dealt to its waves in turn.
+//    The ReLU * w reduction over
 //    heads runs in the epilogue: per lane 4 heads per head tile, then across
 //    the four lane groups.
 //  * idx_prefill_kernel -- the same contraction for many queries: eight waves
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // ---------------------------------------------------------------------------
 // MFMA paths
 // ---------------------------------------------------------------------------
-// One query per grid row; waves split the positions of the work-group.  Each
-// wave streams a contiguous range through a register ring of R key chunks
+// One query per grid row; the query's waves share its positions chunk by
+// chunk.  Each wave streams its chunks through a register ring of R key chunks
 // (16 positions each), so R - 1 chunks (28 KB of bf16 keys per wave at R = 8)
 // stay in flight while one is consumed; R shrinks to 4 where the query block
 // alone takes half the registers (H^I x d^I = 128 x 128).  The loop body is free of conditional memory operations: ring
@@ -119,6 +121,7 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // draining the ring.  The scores (times the fp8 scale) leave with coalesced
 // stores after the loop.
 constexpr int kDecMaxRing = 8;
+constexpr int kDecTargetWgs = 512;  // ~2 waves per SIMD
 constexpr int kDecMaxSpan = 1024;                    // positions per wave, at most
 constexpr int kDecBuf = kDecMaxSpan + 16 * kDecMaxRing;  // + the ring's overrun
 template <int HT, int DI>
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ k, const float* __restrict__ kscale,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kv_len,
-    int T, int L, int s_per_wave, float* __restrict__ scores) {
+    int T, int L, float* __restrict__ scores) {
   constexpr int HI = 16 * HT;
   constexpr int ROWB = FP8 ? DI : 2 * DI;  // bytes per key row
   constexpr int NSC = kDecMaxSpan / 64;    // prefetched scales per lane
@@ -140,56 +143,60 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int lim = candidate_limit(q_pos, kv_len, b, bt, L);
-  const int s_begin = (blockIdx.x * 4 + wave) * s_per_wave;
-  const int s_end = min(s_begin + s_per_wave, L);
-  if (s_begin >= s_end) return;
   float* out = scores + bt * L;
-  const int v_end = min(s_end, lim);  // positions needing a score
-  // positions [max(s_begin, lim), s_end) are not candidates
-  for (int s = max(s_begin, lim) + lane; s < s_end; s += 64) out[s] = -INFINITY;
-  if (s_begin >= v_end) return;
-
+  const int v_end = min(lim, L);  // positions [0, v_end) need a score
+  for (int s = v_end + (int)(blockIdx.x * 256 + threadIdx.x); s < L; s += (int)gridDim.x * 256)
+    out[s] = -INFINITY;
+  // The query's 16-position chunks are dealt to its W waves in turn: wave wq
+  // takes chunks wq, wq + W, wq + 2 W, ..., so the waves sweep the key rows
+  // together (contiguous ranges per wave finished up to a third apart).  A
+  // wave has at most (positions per wave of the grid) / 16 <= 64 chunks.
+  const int W = gridDim.x * 4, wq = blockIdx.x * 4 + wave;
+  const int nch_all = (v_end + 15) / 16;
+  const int nch = wq < nch_all ? (nch_all - wq + W - 1) / W : 0;
+  if (nch == 0) return;
   const uint8_t* kb = k + (int64_t)b * L * ROWB;
-  const int nch = (v_end - s_begin + 15) / 16;
-  auto row_of = [&](int c) { return kb + (int64_t)min(s_begin + 16 * c + n, v_end - 1) * ROWB; };
+  auto pos_of = [&](int c, int j) { return 16 * (wq + c * W) + j; };
+  auto row_of = [&](int c) { return kb + (int64_t)min(pos_of(c, n), v_end - 1) * ROWB; };
 
+  // The query, the weights and the first R chunks go out together; the wait
+  // after the ring's first loads completes the older loads (query, weights,
+  // scales) and leaves the ring in flight.  The loop is then entered, as it is
+  // continued, with exactly the ring's loads outstanding, so each chunk's wait
+  // counts the R - 1 younger chunks.
   QueryRegs<HT, DI, FP8> qr;
   qr.load(q + bt * HI * DI, w + bt * HI, lane);
-  // The query and weights must have landed before the ring starts: loads
-  // still pending at the loop entry would make every iteration's vmcnt wait
-  // count the ring's own loads and drain it.
-  wait_vmcnt<0>();
   float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
   if constexpr (FP8) {
     const float* scb = kscale + (int64_t)b * L;
 #pragma unroll
     for (int i = 0; i < NSC; ++i)
-      scr[i] = scb[min(s_begin + lane + 64 * i, v_end - 1)];
+      scr[i] = scb[min(pos_of(4 * i + (lane >> 4), lane & 15), v_end - 1)];
   }
-  // The ring is filled by the loop itself (its first pass only loads), so the
-  // ring registers are the same on every pass and at the loop entry.
+  asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
   KeyChunk<DI, FP8> ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ring[i].load(row_of(i), g);
+  wait_vmcnt<R * KeyChunk<DI, FP8>::NL>();
   float* sb = sbuf[wave];
-  for (int c0 = -R; c0 < nch; c0 += R) {
+  for (int c0 = 0; c0 < nch; c0 += R) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int c = c0 + i;
-      if (c0 >= 0) {  // uniform; chunks past nch are computed and dropped
-        const float sc = qr.score(ring[i]);
-        sb[16 * c + n] = sc;  // the four lane groups write the same value
-      }
+      const int c = c0 + i;  // chunks past nch are computed and dropped
+      const float sc = qr.score(ring[i]);
+      sb[16 * c + n] = sc;  // the four lane groups write the same value
       ring[i].load(row_of(c + R), g);
     }
   }
-  // the wave's own LDS writes are ordered before these reads
-  const int span = v_end - s_begin;
+  // the wave's own LDS writes are ordered before these reads; slot i of a
+  // lane is position j = lane % 16 of chunk 4 i + lane / 16 (64-byte runs)
 #pragma unroll
   for (int i = 0; i < NSC; ++i) {
-    const int j = lane + 64 * i;
-    if (j < span) {
-      float v = sb[j];
+    const int c = 4 * i + (lane >> 4), s = pos_of(c, lane & 15);
+    if (c < nch && s < v_end) {
+      float v = sb[16 * c + (lane & 15)];
       if constexpr (FP8) v *= scr[i];
-      out[s_begin + j] = v;
+      out[s] = v;
     }
   }
 }
@@ -309,14 +316,14 @@ static hipError_t launch_mfma(const IndexerArgs& a, hipStream_t st) {
         q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, a.scores);
   } else {
     // long per-wave ranges amortise the query registers; shrink them only
-    // until the grid has ~2 waves per SIMD (512 work-groups of 4 waves)
+    // until the grid has kDecTargetWgs work-groups of 4 waves
     int s_per_wave = kDecMaxSpan;
     const int64_t rows = (int64_t)a.B * a.T;
-    while (s_per_wave > 64 && rows * ((a.L + 4 * s_per_wave - 1) / (4 * s_per_wave)) < 512)
+    while (s_per_wave > 64 && rows * ((a.L + 4 * s_per_wave - 1) / (4 * s_per_wave)) < kDecTargetWgs)
       s_per_wave /= 2;
     dim3 grid((a.L + 4 * s_per_wave - 1) / (4 * s_per_wave), (unsigned)rows);
     idx_decode_kernel<HT, DI, FP8><<<grid, 256, 0, st>>>(
-        q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, s_per_wave, a.scores);
+        q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, a.scores);
   }
   return hipGetLastError();
 }
