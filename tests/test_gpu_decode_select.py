@@ -1,0 +1,117 @@
+"""GPU parity of the decode Top-K that reads the score kernel's per-work-group
+candidate lists (sparse_attn_decode and sparse_attn_csa_decode with the MFMA
+indexer).
+
+Whichever way the select goes -- from the lists, or from the score row when
+the lists cannot be trusted (a work-group holding more of the row's top k
+than its floor kept, more kept keys than fit on chip, fewer candidates than k
+with keys dropped) -- the selected set must equal, bit for bit, the oracle's
+top-k of the same scores: those of sparse_attn_indexer_scores, which runs the
+same contraction (its scores are parity-checked against the oracle's indexer
+in test_gpu_parity.py and test_gpu_fullsize.py).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_indexer_sparse_amd import api, workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+H, DC, DR = 64, 512, 64
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", file=sys.stderr, flush=True)
+
+
+def _index_inputs(kind, B, L, seed):
+    """(q_idx [B,1,HI,dI] bf16, w [B,1,HI] f32, k_idx [B,L,dI] bf16) on the CPU."""
+    g = torch.Generator().manual_seed(seed)
+    if kind == "ties":
+        # integers in {-1, 0, 1} and weights in {0, 1}: integer scores, exact
+        # in fp32, with many ties at the k-th score
+        HI, dI = 16, 64
+        q = torch.randint(-1, 2, (B, 1, HI, dI), generator=g).to(torch.bfloat16)
+        w = torch.randint(0, 2, (B, 1, HI), generator=g).float()
+        k = torch.randint(-1, 2, (B, L, dI), generator=g).to(torch.bfloat16)
+        return q, w, k
+    HI, dI = 64, 128
+    q = torch.randn(B, 1, HI, dI, generator=g).to(torch.bfloat16)
+    w = torch.rand(B, 1, HI, generator=g)
+    k = torch.randn(B, L, dI, generator=g).to(torch.bfloat16)
+    if kind == "clustered":
+        # 64-position runs every 8192 positions scaled by 8 (scores scale with
+        # the key, ReLU being positively homogeneous): every score work-group
+        # takes its positions in 64-position runs, so these all land in one
+        # work-group per row, which then holds far more of the top k than its
+        # share
+        pos = torch.arange(L)
+        k[:, (pos % 8192) < 64] *= 8
+    elif kind == "allequal":
+        k[:] = k[:, :1]  # one key row everywhere: every score ties
+    return q, w, k
+
+
+def _check_decode(q, w, k, k_scale, kv_len, topk):
+    B, L = k.shape[0], k.shape[1]
+    gm = torch.Generator(device=DEV).manual_seed(11)
+    q_lat = torch.randn(B, 1, H, DC, device=DEV, generator=gm).to(torch.bfloat16)
+    q_rope = torch.randn(B, 1, H, DR, device=DEV, generator=gm).to(torch.bfloat16)
+    kv = torch.randn(B, L, DC + DR, device=DEV, generator=gm).to(torch.bfloat16)
+    qd, wd, kd = q.to(DEV), w.to(DEV), k.to(DEV)
+    sd = None if k_scale is None else k_scale.to(DEV)
+    kl = None if kv_len is None else kv_len.to(DEV)
+    out, lse, idx = api.sparse_attn_decode(qd, wd, kd, sd, kl, topk, q_lat, q_rope,
+                                           kv[..., :DC], kv[..., DC:], 0.04)
+    s = api.sparse_attn_indexer_scores(qd, wd, kd, k_scale=sd, kv_len=kl)
+    torch.cuda.synchronize()
+    oi, oc = oracle.topk(s.cpu().double().numpy(), topk, kv_len=kv_len)
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, oi), \
+        f"rows differ: {sorted(set(np.nonzero((gi != oi).any(-1))[0].tolist()))}"
+    assert torch.isfinite(out).all().item()
+
+
+@pytest.mark.parametrize("kind,B,L,topk,kv", [
+    ("spread", 4, 32768, 2048, None),
+    ("clustered", 4, 32768, 2048, None),
+    ("clustered", 32, 32768, 2048, None),  # the benchmark's launch geometry
+    ("ties", 3, 20037, 512, None),
+    ("allequal", 2, 10000, 300, None),
+    ("spread", 6, 9000, 2048, [9000, 2047, 2048, 0, 1, 5000]),
+    ("spread", 2, 3000, 4096, None),  # fewer candidates than k
+    ("spread", 2, 131072, 2048, [131072, 100000]),
+])
+def test_decode_select_equals_oracle_topk_of_the_same_scores(kind, B, L, topk, kv):
+    _announce(f"decode select {kind} B={B} L={L} k={topk} kv_len={kv}")
+    q, w, k = _index_inputs(kind, B, L, seed=B * 1000 + L % 997)
+    kv_len = None if kv is None else torch.tensor(kv, dtype=torch.int32)
+    _check_decode(q, w, k, None, kv_len, topk)
+
+
+def test_decode_select_fp8_keys():
+    _announce("decode select fp8 keys B=3 L=40000 k=2048")
+    wl = workloads.decode_128k_fp8(B=3, L=40000)
+    _check_decode(wl.q_idx, wl.w, wl.k_idx, wl.k_scale, wl.kv_len, wl.topk)
+
+
+def test_csa_decode_select_equals_oracle_topk():
+    _announce("csa decode select B=3 Lc=12000 k=1024")
+    B, Lc, k, n_win = 3, 12000, 1024, 128
+    q, w, kidx = _index_inputs("clustered", B, Lc, seed=77)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    qa = torch.randn(B, H, DC, device=DEV, generator=g).to(torch.bfloat16)
+    comp = torch.randn(B, Lc, DC, device=DEV, generator=g).to(torch.bfloat16)
+    win = torch.randn(B, n_win, DC, device=DEV, generator=g).to(torch.bfloat16)
+    n_comp = torch.tensor([Lc, 7000, 1500], dtype=torch.int32)
+    qd, wd, kd, nc = q.to(DEV), w.to(DEV), kidx.to(DEV), n_comp.to(DEV)
+    out, lse, idx = api.sparse_attn_csa_decode(qd[:, 0].contiguous(), wd[:, 0].contiguous(), kd,
+                                               None, nc, k, qa, comp, win, 0.04)
+    s = api.sparse_attn_indexer_scores(qd, wd, kd, kv_len=nc)
+    torch.cuda.synchronize()
+    oi, oc = oracle.topk(s.cpu().double().numpy(), k, kv_len=n_comp)
+    assert np.array_equal(idx.cpu().numpy(), oi[:, 0])

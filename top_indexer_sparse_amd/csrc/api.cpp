@@ -99,7 +99,8 @@ int check_mla(const sa::MlaArgs& a, size_t ws_bytes) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// decode workspace layout: scores [B, L] f32 | idx [B, k] | count [B] | topk ws | mla ws
+// decode workspace layout: scores [B, L] f32 | idx [B, k] | count [B] | topk ws or the
+// indexer's candidate lists | mla ws
 struct DecodeWs {
   size_t scores, idx, count, topk, mla, total;
 };
@@ -113,12 +114,29 @@ DecodeWs decode_ws(int B, int L, int k, int H, int dc, int kv_dtype, int n_win =
   off = align256(off + (size_t)B * k * sizeof(int32_t));
   w.count = off;
   off = align256(off + (size_t)B * sizeof(int32_t));
-  w.topk = off;
-  off = align256(off + sa::topk_workspace_bytes(B, 1, L, k));
+  w.topk = off;  // the top-k's scratch, or the indexer's candidate lists
+  const size_t tk = sa::topk_workspace_bytes(B, 1, L, k), kl = sa::keep_workspace_bytes(B, L);
+  off = align256(off + (tk > kl ? tk : kl));
   w.mla = off;
   off = align256(off + sa::mla_workspace_bytes(kv_dtype, B, 1, k + n_win, H, dc));
   w.total = off;
   return w;
+}
+
+// Scores and Top-K of a decode step (T = 1).  Where the MFMA score kernel
+// runs, it also leaves per-work-group candidate lists in the top-k region of
+// the workspace and the select reads those (falling back to the scores row
+// by itself); otherwise the top-k runs over the scores.
+int index_and_select(sa::IndexerArgs ia, const sa::TopkArgs& ta, void* topk_ws, hipStream_t st) {
+  const bool keep = sa::keep_supported(ia, ta.k);
+  if (keep) ia.keep = sa::keep_layout(topk_ws, ia.B, ia.L, ta.k);
+  int s = hip_status(sa::launch_indexer(ia, st), "decode indexer launch");
+  if (s != SA_OK) return s;
+  if (keep)
+    return hip_status(sa::launch_keep_select(ia.keep, ta.scores, ta.kv_len, ta.B, ta.L, ta.idx,
+                                             ta.count, st),
+                      "decode select launch");
+  return hip_status(sa::launch_topk(ta, st), "decode topk launch");
 }
 
 // Rows longer than the fused select's on-chip row take the staged select in
@@ -267,8 +285,7 @@ int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w, const
     s = fail(SA_ERR_WORKSPACE, "decode: workspace of %zu bytes required, %zu given", lay.total, ws_bytes);
   if (s != SA_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  s = hip_status(sa::launch_indexer(ia, st), "decode indexer launch");
-  if (s == SA_OK) s = hip_status(sa::launch_topk(ta, st), "decode topk launch");
+  s = index_and_select(ia, ta, base + lay.topk, st);
   if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "decode mla launch");
   return s;
 }
@@ -420,8 +437,7 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w, c
   }
   if (s != SA_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  s = hip_status(sa::launch_indexer(ia, st), "csa indexer launch");
-  if (s == SA_OK) s = hip_status(sa::launch_topk(ta, st), "csa topk launch");
+  s = index_and_select(ia, ta, base + lay.topk, st);
   if (s == SA_OK) s = hip_status(sa::launch_mla(ma, st), "csa attention launch");
   return s;
 }

@@ -23,6 +23,7 @@
 #include "common.hpp"
 #include "index_core.hpp"
 #include "launch.hpp"
+#include "split_select.hpp"
 
 namespace sa {
 
@@ -121,18 +122,24 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // draining the ring.  The scores (times the fp8 scale) leave with coalesced
 // stores after the loop.
 constexpr int kDecMaxRing = 8;
-constexpr int kDecTargetWgs = 512;  // ~2 waves per SIMD
-constexpr int kDecMaxSpan = 1024;                    // positions per wave, at most
 constexpr int kDecBuf = kDecMaxSpan + 16 * kDecMaxRing;  // + the ring's overrun
 template <int HT, int DI>
 constexpr int dec_ring() { return 16 * HT * DI >= 16384 ? 4 : kDecMaxRing; }
 
-template <int HT, int DI, bool FP8>
+// With KEEP, the work-group also leaves its candidate list for the Top-K
+// select (IdxKeep): n_w candidates here (positions < lim with a key), of
+// which the row's top k hold about p n_w, p = min(1, k / lim), give or take
+// sqrt(p n_w (1 - p)) when the large scores are spread over the row (the
+// dealing of chunks to waves spreads every 64-position run of a 1024-position
+// stretch over a different work-group).  The work-group keeps its r1 = p n_w
+// + 5 sd + 2 largest keys, rounded down to a bin of a histogram fitted to its
+// key range: every key >= the floor key of that bin.
+template <int HT, int DI, bool FP8, bool KEEP>
 __global__ __launch_bounds__(256) void idx_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint8_t* __restrict__ k, const float* __restrict__ kscale,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ kv_len,
-    int T, int L, float* __restrict__ scores) {
+    int T, int L, float* __restrict__ scores, IdxKeep kp) {
   constexpr int HI = 16 * HT;
   constexpr int ROWB = FP8 ? DI : 2 * DI;  // bytes per key row
   constexpr int NSC = kDecMaxSpan / 64;    // prefetched scales per lane
@@ -154,50 +161,118 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   const int W = gridDim.x * 4, wq = blockIdx.x * 4 + wave;
   const int nch_all = (v_end + 15) / 16;
   const int nch = wq < nch_all ? (nch_all - wq + W - 1) / W : 0;
-  if (nch == 0) return;
+  if (!KEEP && nch == 0) return;  // the candidate list needs every wave
   const uint8_t* kb = k + (int64_t)b * L * ROWB;
   auto pos_of = [&](int c, int j) { return 16 * (wq + c * W) + j; };
   auto row_of = [&](int c) { return kb + (int64_t)min(pos_of(c, n), v_end - 1) * ROWB; };
 
-  // The query, the weights and the first R chunks go out together; the wait
-  // after the ring's first loads completes the older loads (query, weights,
-  // scales) and leaves the ring in flight.  The loop is then entered, as it is
-  // continued, with exactly the ring's loads outstanding, so each chunk's wait
-  // counts the R - 1 younger chunks.
-  QueryRegs<HT, DI, FP8> qr;
-  qr.load(q + bt * HI * DI, w + bt * HI, lane);
   float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
-  if constexpr (FP8) {
-    const float* scb = kscale + (int64_t)b * L;
-#pragma unroll
-    for (int i = 0; i < NSC; ++i)
-      scr[i] = scb[min(pos_of(4 * i + (lane >> 4), lane & 15), v_end - 1)];
-  }
-  asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
-  KeyChunk<DI, FP8> ring[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) ring[i].load(row_of(i), g);
-  wait_vmcnt<R * KeyChunk<DI, FP8>::NL>();
   float* sb = sbuf[wave];
-  for (int c0 = 0; c0 < nch; c0 += R) {
+  if (KEEP ? nch > 0 : true) {
+    // The query, the weights and the first R chunks go out together; the
+    // wait after the ring's first loads completes the older loads (query,
+    // weights, scales) and leaves the ring in flight.  The loop is then
+    // entered, as it is continued, with exactly the ring's loads outstanding,
+    // so each chunk's wait counts the R - 1 younger chunks.
+    QueryRegs<HT, DI, FP8> qr;
+    qr.load(q + bt * HI * DI, w + bt * HI, lane);
+    if constexpr (FP8) {
+      const float* scb = kscale + (int64_t)b * L;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int c = c0 + i;  // chunks past nch are computed and dropped
-      const float sc = qr.score(ring[i]);
-      sb[16 * c + n] = sc;  // the four lane groups write the same value
-      ring[i].load(row_of(c + R), g);
+      for (int i = 0; i < NSC; ++i)
+        scr[i] = scb[min(pos_of(4 * i + (lane >> 4), lane & 15), v_end - 1)];
+    }
+    asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
+    KeyChunk<DI, FP8> ring[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) ring[i].load(row_of(i), g);
+    wait_vmcnt<R * KeyChunk<DI, FP8>::NL>();
+    for (int c0 = 0; c0 < nch; c0 += R) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int c = c0 + i;  // chunks past nch are computed and dropped
+        const float sc = qr.score(ring[i]);
+        sb[16 * c + n] = sc;  // the four lane groups write the same value
+        ring[i].load(row_of(c + R), g);
+      }
     }
   }
   // the wave's own LDS writes are ordered before these reads; slot i of a
   // lane is position j = lane % 16 of chunk 4 i + lane / 16 (64-byte runs)
+  uint32_t key[KEEP ? NSC : 1];
 #pragma unroll
   for (int i = 0; i < NSC; ++i) {
     const int c = 4 * i + (lane >> 4), s = pos_of(c, lane & 15);
-    if (c < nch && s < v_end) {
+    const bool valid = c < nch && s < v_end;
+    if (valid) {
       float v = sb[16 * c + (lane & 15)];
       if constexpr (FP8) v *= scr[i];
       out[s] = v;
+      if constexpr (KEEP) key[i] = score_key(v);
+    } else if constexpr (KEEP) {
+      key[i] = 0u;  // not a candidate
     }
+  }
+  if constexpr (KEEP) {
+    __shared__ __align__(16) int hist[kSpBins];
+    __shared__ int wn[4], nkept;
+    __shared__ uint32_t wmin[4], wmax[4];
+    const int tid = threadIdx.x;
+    // ---- the work-group's candidates and their key range ----
+    int nv = 0;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      nv += key[i] != 0u;
+      mn = key[i] ? min(mn, key[i]) : mn;
+      mx = max(mx, key[i]);
+    }
+    nv = wave_total(nv);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    for (int i = tid; i < kSpBins; i += 256) hist[i] = 0;
+    if (tid == 0) nkept = 0;
+    if (lane == 0) {
+      wn[wave] = nv;
+      wmin[wave] = mn;
+      wmax[wave] = mx;
+    }
+    __syncthreads();
+    const int n_w = wn[0] + wn[1] + wn[2] + wn[3];
+    const uint32_t kmin = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+    const uint32_t kmax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const float p = fminf(1.f, (float)kp.k / (float)max(lim, 1));
+    const float mean = p * (float)n_w;
+    const int r1 = min(n_w, (int)ceilf(mean + 5.f * sqrtf(mean * (1.f - p)) + 2.f));
+    uint32_t lo = kmin;  // all of them
+    if (n_w > r1) {      // uniform over the work-group
+      const int sh = max(0, 32 - __clz(kmax - kmin) - 11);  // (range >> sh) < 2048
+#pragma unroll
+      for (int i = 0; i < NSC; ++i) hist_add(hist, (key[i] - kmin) >> sh, key[i] != 0u);
+      __syncthreads();
+      int bin, above, total;
+      wave_rank_bin(hist, r1, bin, above, total);  // every wave, the same bin
+      lo = kmin + ((uint32_t)bin << sh);
+    }
+    // ---- the keys >= lo, compacted (any order): one LDS atomic per wave ----
+    int nk = 0;
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) nk += key[i] != 0u && key[i] >= lo;
+    const int inc = wave_scan_incl(nk);
+    int wbase = 0;
+    if (lane == 63) wbase = atomicAdd(&nkept, inc);
+    int o = __builtin_amdgcn_readlane(wbase, 63) + inc - nk;
+    const int64_t unit = bt * kp.nwg + blockIdx.x;
+    uint2* dst = kp.keep + unit * kp.cap;
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      if (key[i] != 0u && key[i] >= lo) {
+        dst[o] = make_uint2(key[i], (uint32_t)pos_of(4 * i + (lane >> 4), lane & 15));
+        ++o;
+      }
+    }
+    __syncthreads();  // every wave's count is in
+    if (tid == 0) kp.info[unit] = make_int4(nkept, n_w, (int)lo, (int)kmax);
   }
 }
 
@@ -315,15 +390,15 @@ static hipError_t launch_mfma(const IndexerArgs& a, hipStream_t st) {
     idx_prefill_kernel<HT, DI, FP8><<<grid, 512, 0, st>>>(
         q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, a.scores);
   } else {
-    // long per-wave ranges amortise the query registers; shrink them only
-    // until the grid has kDecTargetWgs work-groups of 4 waves
-    int s_per_wave = kDecMaxSpan;
     const int64_t rows = (int64_t)a.B * a.T;
-    while (s_per_wave > 64 && rows * ((a.L + 4 * s_per_wave - 1) / (4 * s_per_wave)) < kDecTargetWgs)
-      s_per_wave /= 2;
+    const int s_per_wave = dec_span(rows, a.L);
     dim3 grid((a.L + 4 * s_per_wave - 1) / (4 * s_per_wave), (unsigned)rows);
-    idx_decode_kernel<HT, DI, FP8><<<grid, 256, 0, st>>>(
-        q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, a.scores);
+    if (a.keep.info)  // the candidate lists' geometry follows this grid (keep_layout)
+      idx_decode_kernel<HT, DI, FP8, true><<<grid, 256, 0, st>>>(
+          q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, a.scores, a.keep);
+    else
+      idx_decode_kernel<HT, DI, FP8, false><<<grid, 256, 0, st>>>(
+          q, a.w, k, a.k_scale, a.q_pos, a.kv_len, a.T, a.L, a.scores, a.keep);
   }
   return hipGetLastError();
 }

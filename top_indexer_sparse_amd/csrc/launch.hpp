@@ -9,6 +9,17 @@
 
 namespace sa {
 
+// Candidate lists the decode indexer leaves for the Top-K select (few query
+// rows, T = 1): every score work-group keeps the keys of its positions at or
+// above a floor set so that, with high probability, it keeps all of its
+// positions that are in the row's top k.  The select checks that afterwards
+// and reads the score row instead when it does not hold.
+struct IdxKeep {
+  int4* info;   // [rows][nwg]: kept, candidates, floor key, max key
+  uint2* keep;  // [rows][nwg][cap]: (key, position) of the kept keys, any order
+  int nwg, cap, k;
+};
+
 struct IndexerArgs {
   const void* q;
   int q_dtype;
@@ -20,9 +31,31 @@ struct IndexerArgs {
   const int32_t* kv_len;
   int B, T, L, HI, dI;
   float* scores;
+  IdxKeep keep{};  // info == nullptr: scores only
 };
 bool indexer_uses_mfma(const IndexerArgs& a);
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
+
+// Grid of the decode score kernel (few query rows): work-groups of 4 waves,
+// each wave over at most kDecMaxSpan positions; long ranges amortise the
+// query registers, so they are halved only until the grid has kDecTargetWgs
+// work-groups (about 2 waves per SIMD).  Returns positions per wave.
+constexpr int kDecMaxSpan = 1024;
+constexpr int kDecTargetWgs = 512;
+inline int dec_span(int64_t rows, int L) {
+  int s = kDecMaxSpan;
+  while (s > 64 && rows * ((L + 4 * s - 1) / (4 * s)) < kDecTargetWgs) s /= 2;
+  return s;
+}
+
+// The select over the candidate lists (one work-group per row).
+constexpr int kKeepMaxL = 131072;  // row bitmaps held in LDS
+constexpr int kKeepMaxRows = 128;
+bool keep_supported(const IndexerArgs& a, int k);
+size_t keep_workspace_bytes(int64_t rows, int L);
+IdxKeep keep_layout(void* ws, int64_t rows, int L, int k);
+hipError_t launch_keep_select(const IdxKeep& kp, const float* scores, const int32_t* kv_len,
+                              int rows, int L, int32_t* idx, int32_t* count, hipStream_t st);
 
 // Fused prefill select (indexer scores + Top-K, the row held in LDS).
 constexpr int kPrefillSelectMaxL = 32768;

@@ -1,8 +1,9 @@
 // split_select.hpp -- the second phase of the split Top-K (few long rows):
 // from the chunk work-groups' counts and kept keys, the row's k selected
-// positions in ascending order.  Shared by the top-k select kernel and the
-// fused decode's attention kernel, which runs it in its prologue, so both
-// produce the same set by the same code.
+// positions in ascending order.  Its pieces (the radix search for tau over
+// kept keys, the straight row select) also serve the select over the decode
+// indexer's candidate lists, and the histogram helpers the indexer's own
+// floor search, so every path finds tau by the same code.
 //
 // Selection rule ("Sparse Attention 数学学习笔记" §9; "MLA 与稀疏注意力" DSA
 // section, the selected-position helper ordering by (-score, position)):
@@ -116,6 +117,41 @@ __device__ __forceinline__ int sp_block_sum(int x, int* red) {
   return total;
 }
 
+// The bin of `hist` (kSpBins bins, 16-byte aligned) holding rank r counted
+// from the top (1 <= r <= total) and the entries in higher bins, found by one
+// wave on its own: every wave that calls it gets the same answer, with no
+// barrier.  Lane l sums the 32 bins below 2048 - 32 l (its 16-byte reads
+// rotated by lane against bank conflicts); the wave then reads the 32 bins of
+// the lane holding rank r, one per lane from the top, and a prefix scan over
+// them names the bin.  total = all entries; bin = -1 when r > total.
+__device__ __forceinline__ void wave_rank_bin(const int* hist, int r, int& bin, int& above,
+                                              int& total) {
+  const int lane = lane_id();
+  const int base = kSpBins - 32 * (lane + 1);
+  int own = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int4 v = *(const int4*)(hist + base + 4 * ((q + lane) & 7));
+    own += v.x + v.y + v.z + v.w;
+  }
+  const int incl = wave_scan_incl(own);
+  total = __builtin_amdgcn_readlane(incl, 63);
+  const int ab = incl - own;  // entries in the bins above this lane's
+  const uint64_t m = __ballot(ab < r && r <= incl);
+  bin = -1;
+  above = 0;
+  if (m == 0) return;
+  const int src = __ffsll((unsigned long long)m) - 1;
+  const int sbase = __builtin_amdgcn_readlane(base, src);
+  const int sab = __builtin_amdgcn_readlane(ab, src);
+  const int h = lane < 32 ? hist[sbase + 31 - lane] : 0;  // lane i: i-th bin from the top
+  const int hi = wave_scan_incl(h);
+  const uint64_t mm = __ballot(lane < 32 && sab + hi - h < r && r <= sab + hi);
+  const int f = __ffsll((unsigned long long)mm) - 1;
+  bin = sbase + 31 - f;
+  above = sab + __builtin_amdgcn_readlane(hi - h, f);
+}
+
 // What the first phase left in the workspace, per (row, chunk).
 struct SplitView {
   const float* scores;      // [rows][L] (the fallback reads the row itself)
@@ -140,6 +176,130 @@ struct SplitSmem {
   int* nsmall;     // [1]
 };
 
+// tau, the krem-th largest of the kept keys that lie in [lo, hi] (ranks
+// counted from the top), and need_eq, how many of the keys equal to tau are
+// taken: radix passes over the offsets key - lo, 11 bits at a time from the
+// top, until at most 64 keys share the current bin; one wave then ranks those
+// directly.  Thread t holds its kept keys in rk[0, s) (0: none; kept keys are
+// >= lo >= 1).  Run by all NT threads; 1 <= krem <= the keys in [lo, hi].
+template <int NT, int RUN>
+__device__ __forceinline__ void kept_tau(const uint32_t (&rk)[RUN], int s, uint32_t lo,
+                                         uint32_t hi, int krem, const SplitSmem& sm,
+                                         uint32_t& tau_out, int& need_out) {
+  const int tid = threadIdx.x;
+  int* const red = sm.red;
+  int* const found = sm.found;
+  uint32_t prefix = 0u, pmask = 0u;
+  const uint32_t span = hi - lo;
+  int top = span ? 31 - __clz(span) : -1;
+#pragma unroll 1
+  while (top >= 0) {
+    const int width = min(11, top + 1);
+    const int s2 = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    __syncthreads();  // previous bins read
+    for (int i = tid; i < kSpBins; i += NT) sm.hist[i] = 0;
+    if (tid == 0) *sm.nsmall = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < RUN; ++e) {  // key 0 (none) is below lo >= 1
+      if (e >= s) break;              // uniform
+      const uint32_t c = rk[e] - lo;
+      hist_add(sm.hist, (c >> s2) & dmask, rk[e] >= lo && rk[e] <= hi && (c & pmask) == prefix);
+    }
+    sp_rank_bin<NT>(sm.hist, krem, red, found);
+    prefix |= (uint32_t)found[0] << s2;
+    pmask |= dmask << s2;
+    krem -= found[1];
+    top = s2 - 1;
+    if (top >= 0 && sm.hist[found[0]] <= 64) {
+      // few keys left in the bin: one wave ranks them directly
+#pragma unroll
+      for (int e = 0; e < RUN; ++e) {
+        if (e >= s) break;  // uniform
+        if (rk[e] >= lo && rk[e] <= hi && ((rk[e] - lo) & pmask) == prefix)
+          sm.small[atomicAdd(sm.nsmall, 1)] = rk[e];
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const int n = *sm.nsmall;
+        const uint32_t x = tid < n ? sm.small[tid] : 0u;  // kept keys are >= lo >= 1
+        int gt = 0, eq = 0;
+        for (int i = 0; i < n; ++i) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
+          gt += y > x;
+          eq += y == x;
+        }
+        const uint64_t hit = __ballot(tid < n && gt < krem && krem <= gt + eq);
+        const int lead = __ffsll((unsigned long long)hit) - 1;
+        if (tid == lead) {
+          sm.small[64] = x;
+          sm.small[65] = (uint32_t)(krem - gt);
+        }
+      }
+      __syncthreads();
+      tau_out = sm.small[64];
+      need_out = (int)sm.small[65];
+      return;
+    }
+  }
+  tau_out = lo + prefix;
+  need_out = krem;
+}
+
+// The row's selected positions straight from its scores (candidates: the V
+// positions < lim with a key): radix passes over all its keys find tau when
+// V > k, then the emission walks the row in position order, NT positions per
+// round, passing emit(slot, position).  Run by all NT threads.
+template <int NT, class Emit>
+__device__ __forceinline__ void row_select(const float* srow, int k, int lim, int V,
+                                           const SplitSmem& sm, Emit&& emit) {
+  const int tid = threadIdx.x;
+  int* const red = sm.red;
+  int* const found = sm.found;
+  // ---- straight from the row: radix passes over all its keys ----
+  uint32_t tau = 0u;  // V <= k: every candidate (key > 0) is taken
+  int need_eq = 0;
+  if (V > k) {
+    int krem = k;
+    uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int s2 = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+      const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
+      __syncthreads();
+      for (int i = tid; i < kSpBins; i += NT) sm.hist[i] = 0;
+      __syncthreads();
+#pragma unroll 1
+      for (int q0 = 0; q0 < lim; q0 += NT) {
+        const int q = q0 + tid;
+        const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
+        hist_add(sm.hist, (c >> s2) & dmask, c != 0u && (c & pmask) == prefix);
+      }
+      sp_rank_bin<NT>(sm.hist, krem, red, found);
+      prefix |= (uint32_t)found[0] << s2;
+      pmask |= dmask << s2;
+      krem -= found[1];
+    }
+    tau = prefix;
+    need_eq = krem;
+  }
+  // emission in position order, NT positions per round
+  int run_gt = 0, run_eq = 0;
+#pragma unroll 1
+  for (int q0 = 0; q0 < lim; q0 += NT) {
+    const int q = q0 + tid;
+    const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
+    const int g = c != 0u && c > tau, eq = c != 0u && c == tau;
+    int total;
+    const int before = sp_scan_excl<NT>((g << 16) | eq, red, total);
+    const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
+    if (g || (eq && eqb < need_eq)) emit(gtb + min(eqb, need_eq), q);
+    run_gt += total >> 16;
+    run_eq += total & 0xffff;
+  }
+}
+
 // The selected positions of row `row` (candidates: positions < lim with a
 // key), each passed to emit(slot, position) with its ascending output slot
 // slot < min(k, #candidates), which is returned.  loaded() runs once the
@@ -155,7 +315,6 @@ __device__ __forceinline__ int split_select(const SplitView& v, int64_t row, int
   const int tid = threadIdx.x;
   const int nch = min(v.nchunk, (lim + kSpChunk - 1) / kSpChunk);
   int* const red = sm.red;
-  int* const found = sm.found;
 
   // ---- the chunks' counts -> offsets of their kept keys ----
   {
@@ -229,72 +388,10 @@ __device__ __forceinline__ int split_select(const SplitView& v, int64_t row, int
       if (e >= s) break;  // uniform
       rk[e] = j0 + e < K ? sm.kk[j0 + e] : 0u;  // 0: none
     }
-    // ---- tau: the (k - A)-th largest inside key, by radix passes over the
-    //      offsets key - lo (11 bits at a time, from the top) ----
-    int krem = k - A;
-    uint32_t prefix = 0u, pmask = 0u;
-    const uint32_t span = hi - lo;
-    int top = span ? 31 - __clz(span) : -1;
-    uint32_t tau = 0u;
-    int need_eq = 0;
-    bool done = false;
-#pragma unroll 1
-    while (top >= 0) {
-      const int width = min(11, top + 1);
-      const int s2 = top + 1 - width;
-      const uint32_t dmask = (1u << width) - 1u;
-      __syncthreads();  // previous bins read
-      for (int i = tid; i < kSpBins; i += NT) sm.hist[i] = 0;
-      if (tid == 0) *sm.nsmall = 0;
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < kRun; ++e) {  // key 0 (none) is below lo >= 1
-        if (e >= s) break;               // uniform
-        const uint32_t c = rk[e] - lo;
-        hist_add(sm.hist, (c >> s2) & dmask,
-                 rk[e] >= lo && rk[e] <= hi && (c & pmask) == prefix);
-      }
-      sp_rank_bin<NT>(sm.hist, krem, red, found);
-      prefix |= (uint32_t)found[0] << s2;
-      pmask |= dmask << s2;
-      krem -= found[1];
-      top = s2 - 1;
-      if (top >= 0 && sm.hist[found[0]] <= 64) {
-        // few keys left in the bin: one wave ranks them directly
-#pragma unroll
-        for (int e = 0; e < kRun; ++e) {
-          if (e >= s) break;  // uniform
-          if (rk[e] >= lo && rk[e] <= hi && ((rk[e] - lo) & pmask) == prefix)
-            sm.small[atomicAdd(sm.nsmall, 1)] = rk[e];
-        }
-        __syncthreads();
-        if (tid < 64) {
-          const int n = *sm.nsmall;
-          const uint32_t x = tid < n ? sm.small[tid] : 0u;  // kept keys are >= lo >= 1
-          int gt = 0, eq = 0;
-          for (int i = 0; i < n; ++i) {
-            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
-            gt += y > x;
-            eq += y == x;
-          }
-          const uint64_t hit = __ballot(tid < n && gt < krem && krem <= gt + eq);
-          const int lead = __ffsll((unsigned long long)hit) - 1;
-          if (tid == lead) {
-            sm.small[64] = x;
-            sm.small[65] = (uint32_t)(krem - gt);
-          }
-        }
-        __syncthreads();
-        tau = sm.small[64];
-        need_eq = (int)sm.small[65];
-        done = true;
-        break;
-      }
-    }
-    if (!done) {
-      tau = lo + prefix;
-      need_eq = krem;
-    }
+    // ---- tau: the (k - A)-th largest inside key ----
+    uint32_t tau;
+    int need_eq;
+    kept_tau<NT>(rk, s, lo, hi, k - A, sm, tau, need_eq);
     // ---- ascending output: thread t counts its run's selected keys, a
     //      block scan gives their slots ----
     int c = 0;
@@ -316,48 +413,7 @@ __device__ __forceinline__ int split_select(const SplitView& v, int64_t row, int
     }
   } else {
     loaded();
-    // ---- straight from the row: radix passes over all its keys ----
-    const float* srow = v.scores + row * v.L;
-    uint32_t tau = 0u;  // V <= k: every candidate (key > 0) is taken
-    int need_eq = 0;
-    if (V > k) {
-      int krem = k;
-      uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll 1
-      for (int pass = 0; pass < 3; ++pass) {
-        const int s2 = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-        const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-        __syncthreads();
-        for (int i = tid; i < kSpBins; i += NT) sm.hist[i] = 0;
-        __syncthreads();
-#pragma unroll 1
-        for (int q0 = 0; q0 < lim; q0 += NT) {
-          const int q = q0 + tid;
-          const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
-          hist_add(sm.hist, (c >> s2) & dmask, c != 0u && (c & pmask) == prefix);
-        }
-        sp_rank_bin<NT>(sm.hist, krem, red, found);
-        prefix |= (uint32_t)found[0] << s2;
-        pmask |= dmask << s2;
-        krem -= found[1];
-      }
-      tau = prefix;
-      need_eq = krem;
-    }
-    // emission in position order, NT positions per round
-    int run_gt = 0, run_eq = 0;
-#pragma unroll 1
-    for (int q0 = 0; q0 < lim; q0 += NT) {
-      const int q = q0 + tid;
-      const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
-      const int g = c != 0u && c > tau, eq = c != 0u && c == tau;
-      int total;
-      const int before = sp_scan_excl<NT>((g << 16) | eq, red, total);
-      const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
-      if (g || (eq && eqb < need_eq)) emit(gtb + min(eqb, need_eq), q);
-      run_gt += total >> 16;
-      run_eq += total & 0xffff;
-    }
+    row_select<NT>(v.scores + row * v.L, k, lim, V, sm, emit);
   }
   __syncthreads();
   return n_sel;

@@ -646,6 +646,291 @@ __global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) 
   if (a.count && tid == 0) a.count[row] = n_sel;
 }
 
+// ---------------------------------------------------------------------------
+// Select over the decode indexer's candidate lists (IdxKeep), one NT-thread
+// work-group per row.  Every list is read by a team of NT / nwg threads.
+//  1. One round of loads: each team reads its list's counts and floor and a
+//     first batch of its entries (the rest, rarely needed, in a second round).
+//     One barrier gives the totals and, from a scan over the team leaders'
+//     counts, every team its list's offset.
+//  2. tau = the k-th largest kept key.  It is the row's k-th largest key when
+//     it is at least every floor of a list that dropped keys (each such list
+//     then holds all of its positions with a key >= tau, so the kept keys >=
+//     tau are all of the row's): only the C kept keys >= lo0 = the largest
+//     such floor can be tau, and the kept keys are a valid source iff C >= k.
+//     Storing the entries also fills a histogram of those keys on a digit
+//     fitted to [lo0, max key]; after one barrier every wave finds tau's bin
+//     in it (wave_rank_bin) and, when the bin holds at most 64 keys, their
+//     holders gather them (one more barrier) and every wave ranks them.  A
+//     fuller bin takes radix passes over the kept keys (kept_tau).  When the lists are no valid
+//     source, or hold more keys than LDS does, the row's scores are read
+//     directly (row_select).
+//  3. The selected positions are marked in two bitmaps of the row (keys >
+//     tau, keys == tau); a block scan of the bitmap words' counts in position
+//     order gives every selected position its ascending slot and every tie its
+//     rank among the ties (the lowest need_eq positions are taken).
+// ---------------------------------------------------------------------------
+constexpr int kKpThreads = 512;
+constexpr int kKpKeep = 12288;  // kept keys held in LDS
+constexpr int kKpSpec = 12;     // entries per thread in the first round of loads
+constexpr int kKpWords = kKeepMaxL / 32;
+static_assert(kKpWords % kKpThreads == 0 && kKpKeep < 65536 && kTopkMaxK < 65536,
+              "bitmap words per thread; packed counts");
+
+struct KeepSelArgs {
+  IdxKeep kp;
+  const float* scores;
+  const int32_t* kv_len;
+  int L;
+  int32_t* idx;
+  int32_t* count;
+};
+
+__global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArgs a) {
+  constexpr int NT = kKpThreads, NWV = NT / 64;
+  constexpr int kRun = (kKpKeep + NT - 1) / NT;  // kept keys per thread (kept_tau)
+  constexpr int kWpt = kKpWords / NT;            // bitmap words per thread, at most
+  __shared__ uint32_t kk[kKpKeep];
+  __shared__ int32_t kpos[kKpKeep];
+  __shared__ uint32_t gtm[kKpWords], eqm[kKpWords];
+  __shared__ __align__(16) int hist[kSpBins];
+  __shared__ int red[NWV], found[3];
+  __shared__ int wk[NWV], wc[NWV], wt[NWV];
+  __shared__ uint32_t wlo[NWV], whi[NWV], wmx[NWV];
+  __shared__ uint32_t small[66];
+  __shared__ int nsmall;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int lim = candidate_limit(nullptr, a.kv_len, (int)row, row, a.L);
+  const int nwg = a.kp.nwg, cap = a.kp.cap, k = a.kp.k;
+  int32_t* out = a.idx + row * k;
+  const SplitSmem sm{kk, kpos, hist, red, found, nullptr, nullptr, small, &nsmall};
+
+  // ---- 1. one round of loads ----
+  const int tpw = NT / nwg;  // >= 1
+  const int j = tid / tpw, r = tid % tpw;
+  const bool member = j < nwg;
+  int4 inf = make_int4(0, 0, 0, 0);
+  if (member) inf = a.kp.info[row * nwg + j];  // the team's list (one address per team)
+  const uint2* src = a.kp.keep + (row * nwg + min(j, nwg - 1)) * (int64_t)cap;
+  uint2 ent[kKpSpec];  // entries past the list's count are read and dropped
+#pragma unroll
+  for (int m = 0; m < kKpSpec; ++m) ent[m] = src[min(r + tpw * m, cap - 1)];
+  const int NW = (lim + 31) >> 5;
+  for (int i = tid; i < NW; i += NT) gtm[i] = eqm[i] = 0u;
+  for (int i = tid; i < kSpBins; i += NT) hist[i] = 0;
+  if (tid == 0) nsmall = 0;
+
+  // ---- totals, floors, the largest key; the leaders' counts scanned ----
+  const bool lead = member && r == 0;
+  const int nj = inf.x;  // this team's list: kept keys
+  const int kept = lead ? nj : 0, cand = lead ? inf.y : 0;
+  const uint32_t flo = lead && kept > 0 ? (uint32_t)inf.z : 0xffffffffu;
+  const uint32_t fhi = lead && kept < cand ? (uint32_t)inf.z : 0u;  // the list dropped keys
+  const uint32_t kmx = lead ? (uint32_t)inf.w : 0u;
+  const int incl = wave_scan_incl(kept);
+  const int wcand = wave_total(cand);
+  const uint32_t wflo = wave_min_u32(flo), wfhi = wave_max_u32(fhi), wkmx = wave_max_u32(kmx);
+  if (lane == 63) wk[wave] = incl;
+  if (lane == 0) {
+    wc[wave] = wcand;
+    wlo[wave] = wflo;
+    whi[wave] = wfhi;
+    wmx[wave] = wkmx;
+  }
+  __syncthreads();
+  int before = 0, K = 0, V = 0;
+  uint32_t lomin = 0xffffffffu, lomax = 0u, kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    before += w < wave ? wk[w] : 0;
+    K += wk[w];
+    V += wc[w];
+    lomin = min(lomin, wlo[w]);
+    lomax = max(lomax, whi[w]);
+    kmax = max(kmax, wmx[w]);
+  }
+  // lists up to this team's, minus its own (its leader is the team's first thread)
+  const int d0 = before + incl - (member ? nj : 0);
+  const int n_sel = min(k, V);
+  // V <= k: every candidate is taken, which the lists give when none dropped a key
+  bool fast = V > k ? K >= k && K <= kKpKeep : K == V;
+  uint32_t tau = 0u;  // V <= k: every kept key (>= 1) is above it
+  int need_eq = 0;
+  if (fast) {
+    const uint32_t lo0 = max(lomax, lomin);
+    const int sh = max(0, 32 - __clz(kmax - lo0) - 11);  // (range >> sh) < 2048
+    // ---- 2. entries into LDS, keys >= lo0 into the histogram ----
+#pragma unroll
+    for (int m = 0; m < kKpSpec; ++m) {
+      const int i = r + tpw * m;
+      const bool v = member && i < nj;
+      if (v) {
+        kk[d0 + i] = ent[m].x;
+        kpos[d0 + i] = (int32_t)ent[m].y;
+      }
+      hist_add(hist, (ent[m].x - lo0) >> sh, v && ent[m].x >= lo0);
+    }
+    if (member) {
+      for (int i = r + tpw * kKpSpec; i < nj; i += tpw) {
+        const uint2 e = src[i];
+        kk[d0 + i] = e.x;
+        kpos[d0 + i] = (int32_t)e.y;
+        if (e.x >= lo0) atomicAdd(&hist[(e.x - lo0) >> sh], 1);
+      }
+    }
+    __syncthreads();  // kept keys stored, histogram complete
+    if (V > k) {
+      int bin, above, C;
+      wave_rank_bin(hist, k, bin, above, C);
+      fast = C >= k;  // uniform: the same histogram in every wave
+      if (fast && hist[bin] <= 64) {
+        // the keys of tau's bin: their holders append them to `small` (one
+        // LDS atomic per wave), then every wave ranks them against each other
+        auto in_bin = [&](uint32_t x) { return x >= lo0 && (int)((x - lo0) >> sh) == bin; };
+        int nmine = 0;
+#pragma unroll
+        for (int m = 0; m < kKpSpec; ++m)
+          nmine += member && r + tpw * m < nj && in_bin(ent[m].x);
+        if (member)
+          for (int i = r + tpw * kKpSpec; i < nj; i += tpw) nmine += in_bin(kk[d0 + i]);
+        const int minc = wave_scan_incl(nmine);
+        int sbase = 0;
+        if (lane == 63 && minc) sbase = atomicAdd(&nsmall, minc);
+        int o = __builtin_amdgcn_readlane(sbase, 63) + minc - nmine;
+        if (nmine) {
+#pragma unroll
+          for (int m = 0; m < kKpSpec; ++m)
+            if (member && r + tpw * m < nj && in_bin(ent[m].x)) small[o++] = ent[m].x;
+          if (member)
+            for (int i = r + tpw * kKpSpec; i < nj; i += tpw)
+              if (in_bin(kk[d0 + i])) small[o++] = kk[d0 + i];
+        }
+        __syncthreads();
+        const int nb = nsmall;  // == hist[bin] <= 64
+        const int krem = k - above;
+        const uint32_t x = lane < nb ? small[lane] : 0u;
+        int gt = 0, eq = 0;
+        for (int i = 0; i < nb; ++i) {
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
+          gt += y > x;
+          eq += y == x;
+        }
+        const uint64_t hit = __ballot(lane < nb && gt < krem && krem <= gt + eq);
+        const int ld = __ffsll((unsigned long long)hit) - 1;
+        tau = (uint32_t)__builtin_amdgcn_readlane((int)x, ld);
+        need_eq = krem - __builtin_amdgcn_readlane(gt, ld);
+      } else if (fast) {
+        // a crowded bin: radix passes over the kept keys >= lo0
+        const int s = (K + NT - 1) / NT;  // <= kRun
+        const int j0 = tid * s;
+        uint32_t rk[kRun];
+#pragma unroll
+        for (int e = 0; e < kRun; ++e) {
+          if (e >= s) break;  // uniform
+          rk[e] = j0 + e < K ? kk[j0 + e] : 0u;
+        }
+        kept_tau<NT>(rk, s, lo0, kmax, k, sm, tau, need_eq);
+      }
+    }
+    if (fast) {
+      // ---- 3. bitmaps (each team marks its own entries), then slots ----
+#pragma unroll
+      for (int m = 0; m < kKpSpec; ++m) {
+        const int i = r + tpw * m;
+        if (member && i < nj && ent[m].x >= tau) {
+          const int p = (int)ent[m].y;
+          atomicOr(ent[m].x > tau ? &gtm[p >> 5] : &eqm[p >> 5], 1u << (p & 31));
+        }
+      }
+      if (member) {
+        for (int i = r + tpw * kKpSpec; i < nj; i += tpw) {
+          const uint32_t x = kk[d0 + i];
+          const int p = kpos[d0 + i];
+          if (x >= tau) atomicOr(x > tau ? &gtm[p >> 5] : &eqm[p >> 5], 1u << (p & 31));
+        }
+      }
+      __syncthreads();
+      const int wpt = (NW + NT - 1) / NT;  // <= kWpt
+      const int w0 = tid * wpt;
+      uint32_t gw[kWpt], ew[kWpt];
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < kWpt; ++i) {
+        if (i >= wpt) break;  // uniform
+        const int wd = w0 + i;
+        gw[i] = wd < NW ? gtm[wd] : 0u;
+        ew[i] = wd < NW ? eqm[wd] : 0u;
+        c += (__popc(gw[i]) << 16) + __popc(ew[i]);
+      }
+      // keys > tau < k and ties <= K: 16 bits each
+      const int ci = wave_scan_incl(c);
+      if (lane == 63) wt[wave] = ci;
+      __syncthreads();
+      int bef = ci - c;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) bef += w < wave ? wt[w] : 0;
+      int gtb = bef >> 16, eqb = bef & 0xffff;
+#pragma unroll
+      for (int i = 0; i < kWpt; ++i) {
+        if (i >= wpt) break;  // uniform
+        uint32_t m = gw[i] | ew[i];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1u;
+          const int p = 32 * (w0 + i) + bit;
+          if ((gw[i] >> bit) & 1u) {
+            out[gtb + min(eqb, need_eq)] = p;
+            ++gtb;
+          } else {
+            if (eqb < need_eq) out[gtb + eqb] = p;
+            ++eqb;
+          }
+        }
+      }
+    }
+  }
+  if (!fast)
+    row_select<NT>(a.scores + row * a.L, k, lim, V, sm, [&](int slot, int pos) { out[slot] = pos; });
+  for (int i = n_sel + tid; i < k; i += NT) out[i] = -1;
+  if (a.count && tid == 0) a.count[row] = n_sel;
+}
+
+bool keep_supported(const IndexerArgs& a, int k) {
+  if (!indexer_uses_mfma(a) || a.q_pos || a.T != 1 || k < 1 || k > kTopkMaxK) return false;
+  const int64_t rows = (int64_t)a.B;
+  if (rows < 1 || rows > kKeepMaxRows || a.L < 1 || a.L > kKeepMaxL) return false;
+  const int s = dec_span(rows, a.L);
+  return (a.L + 4 * s - 1) / (4 * s) <= kKpThreads;  // one team of threads per list
+}
+
+size_t keep_workspace_bytes(int64_t rows, int L) {
+  if (rows < 1 || L < 1) return 0;
+  const int s = dec_span(rows, L);
+  const int64_t nwg = (L + 4 * s - 1) / (4 * s);
+  return (size_t)(rows * nwg) * sizeof(int4) + 256 + (size_t)(rows * nwg) * 4 * s * sizeof(uint2);
+}
+
+IdxKeep keep_layout(void* ws, int64_t rows, int L, int k) {
+  const int s = dec_span(rows, L);
+  IdxKeep kp{};
+  kp.nwg = (L + 4 * s - 1) / (4 * s);
+  kp.cap = 4 * s;
+  kp.k = k;
+  kp.info = (int4*)ws;
+  const size_t ib = ((size_t)(rows * kp.nwg) * sizeof(int4) + 255) & ~(size_t)255;
+  kp.keep = (uint2*)((char*)ws + ib);
+  return kp;
+}
+
+hipError_t launch_keep_select(const IdxKeep& kp, const float* scores, const int32_t* kv_len,
+                              int rows, int L, int32_t* idx, int32_t* count, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const KeepSelArgs sa{kp, scores, kv_len, L, idx, count};
+  topk_keep_select_kernel<<<(unsigned)rows, kKpThreads, 0, st>>>(sa);
+  return hipGetLastError();
+}
+
 static bool topk_split(int64_t rows, int L) { return rows <= kSpMaxRows && L >= kSpMinL &&
                                                      (L + kSpChunk - 1) / kSpChunk <= kSpMaxChunks; }
 
