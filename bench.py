@@ -103,7 +103,8 @@ def cpu_baseline(wl, budget_s=20.0):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_32k_traffic.md")
 # the decode score kernel's source: its translation unit and the headers it uses
 INDEXER_SRC = [os.path.join(ROOT, "top_indexer_sparse_amd", "csrc", f)
-               for f in ("indexer.hip", "index_core.hpp", "common.hpp")]
+               for f in ("indexer.hip", "index_core.hpp", "split_select.hpp", "select_core.hpp",
+                         "launch.hpp", "common.hpp")]
 
 
 def indexer_source_sha256():
