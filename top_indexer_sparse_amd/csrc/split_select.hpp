@@ -172,7 +172,7 @@ struct SplitSmem {
   int* found;      // [3]
   int* preK;       // [kSpMaxChunks + 1]
   int* tot;        // [4]
-  uint32_t* small; // [66]
+  uint32_t* small; // [68], 16-byte aligned
   int* nsmall;     // [1]
 };
 
@@ -224,11 +224,14 @@ __device__ __forceinline__ void kept_tau(const uint32_t (&rk)[RUN], int s, uint3
       if (tid < 64) {
         const int n = *sm.nsmall;
         const uint32_t x = tid < n ? sm.small[tid] : 0u;  // kept keys are >= lo >= 1
+        // each lane compares its key with all n keys, four per (broadcast) read
         int gt = 0, eq = 0;
-        for (int i = 0; i < n; ++i) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
-          gt += y > x;
-          eq += y == x;
+        for (int i0 = 0; i0 < n; i0 += 4) {
+          const uint4 y = *(const uint4*)(sm.small + i0);
+          gt += (y.x > x) + (i0 + 1 < n && y.y > x) + (i0 + 2 < n && y.z > x) +
+                (i0 + 3 < n && y.w > x);
+          eq += (y.x == x) + (i0 + 1 < n && y.y == x) + (i0 + 2 < n && y.z == x) +
+                (i0 + 3 < n && y.w == x);
         }
         const uint64_t hit = __ballot(tid < n && gt < krem && krem <= gt + eq);
         const int lead = __ffsll((unsigned long long)hit) - 1;

@@ -631,7 +631,7 @@ __global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) 
   __shared__ int found[3];
   __shared__ int preK[kSpMaxChunks + 1];
   __shared__ int tot[4];
-  __shared__ uint32_t small[66];
+  __shared__ __align__(16) uint32_t small[68];
   __shared__ int nsmall;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
   __shared__ int red[NWV], found[3];
   __shared__ int wk[NWV], wc[NWV], wt[NWV];
   __shared__ uint32_t wlo[NWV], whi[NWV], wmx[NWV];
-  __shared__ uint32_t small[66];
+  __shared__ __align__(16) uint32_t small[68];  // 64 keys read 16 bytes at a time, + 2 results
   __shared__ int nsmall;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -810,11 +810,15 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
         const int nb = nsmall;  // == hist[bin] <= 64
         const int krem = k - above;
         const uint32_t x = lane < nb ? small[lane] : 0u;
+        // every lane compares its key with all nb keys, read four at a time
+        // (the same LDS words for every lane: broadcast reads)
         int gt = 0, eq = 0;
-        for (int i = 0; i < nb; ++i) {
-          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
-          gt += y > x;
-          eq += y == x;
+        for (int i0 = 0; i0 < nb; i0 += 4) {
+          const uint4 y = *(const uint4*)(small + i0);
+          gt += (y.x > x) + (i0 + 1 < nb && y.y > x) + (i0 + 2 < nb && y.z > x) +
+                (i0 + 3 < nb && y.w > x);
+          eq += (y.x == x) + (i0 + 1 < nb && y.y == x) + (i0 + 2 < nb && y.z == x) +
+                (i0 + 3 < nb && y.w == x);
         }
         const uint64_t hit = __ballot(lane < nb && gt < krem && krem <= gt + eq);
         const int ld = __ffsll((unsigned long long)hit) - 1;
