@@ -43,7 +43,7 @@ constexpr int kBlkMaxRanges = kBlkMaxSel + 2;
 bool block_supported(const BlockArgs& a) {
   const int G = a.Hq / a.Hkv;
   return a.d == kBlkD && (a.blk == 32 || a.blk == 64 || a.blk == 128) &&
-         (G == 1 || G == 2 || G == 4 || G == 8) && a.nsel >= 1 && a.nsel <= kBlkMaxSel &&
+         (G == 1 || G == 2 || G == 4 || G == kBlkMaxGroup) && a.nsel >= 1 && a.nsel <= kBlkMaxSel &&
          a.L / a.blk <= kBlkMaxBlocks;
 }
 
