@@ -176,7 +176,15 @@ int sparse_attn_mla_forward(const void* q_lat, const void* q_rope, int q_dtype,
  * h_t -> (q^I, w^I) -> {I_t,j} -> S_t -> {c_j : j in S_t} -> o_t).
  * Arguments as in the three stages with T = 1 and q_pos = NULL.
  *   idx_out [B, k] int32 (may be NULL): the selected set, ascending, -1 padded.
- * ws: sparse_attn_workspace_bytes(SA_OP_DECODE, B, 1, L, k, H, dc).
+ * The selected set is the one sparse_attn_topk returns for the scores that
+ * sparse_attn_indexer_scores computes, with the same tie rule.  When the
+ * indexer runs on matrix cores (bf16 queries, H^I in {16, 32, 64, 128}) and
+ * L <= 131072, B <= 128, the score kernel also leaves per-work-group
+ * candidate lists in the workspace and the selection reads those, checking
+ * that they hold every selected position and otherwise reading the scores.
+ * ws: sparse_attn_workspace_bytes(SA_OP_DECODE, B, 1, L, k, H, dc): the scores,
+ *   the index sets, the candidate lists or the Top-K scratch, and the MLA's
+ *   split partials; its contents need no initialisation and are overwritten.
  * ------------------------------------------------------------------------- */
 int sparse_attn_decode(const void* q_idx, int q_idx_dtype, const float* w,
                        const void* k_idx, int k_dtype, const float* k_scale,
