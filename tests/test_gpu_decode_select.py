@@ -85,6 +85,11 @@ def _check_decode(q, w, k, k_scale, kv_len, topk):
     ("spread", 6, 9000, 2048, [9000, 2047, 2048, 0, 1, 5000]),
     ("spread", 2, 3000, 4096, None),  # fewer candidates than k
     ("spread", 2, 131072, 2048, [131072, 100000]),
+    # every key equal: each list keeps all of its keys, 40000 in all, more
+    # than the select holds on chip, so it reads the score row
+    ("allequal", 2, 40000, 2048, None),
+    # one short list per row; rows shorter than k, a single position, k = 64
+    ("spread", 5, 777, 64, [777, 500, 64, 63, 1]),
 ])
 def test_decode_select_equals_oracle_topk_of_the_same_scores(kind, B, L, topk, kv):
     _announce(f"decode select {kind} B={B} L={L} k={topk} kv_len={kv}")
