@@ -28,7 +28,7 @@ def _announce(msg):
     print(f"\n[case] {msg}", file=sys.stderr, flush=True)
 
 
-def _index_inputs(kind, B, L, seed):
+def _index_inputs(kind, B, L, seed, HI=64, dI=128):
     """(q_idx [B,1,HI,dI] bf16, w [B,1,HI] f32, k_idx [B,L,dI] bf16) on the CPU."""
     g = torch.Generator().manual_seed(seed)
     if kind == "ties":
@@ -39,7 +39,6 @@ def _index_inputs(kind, B, L, seed):
         w = torch.randint(0, 2, (B, 1, HI), generator=g).float()
         k = torch.randint(-1, 2, (B, L, dI), generator=g).to(torch.bfloat16)
         return q, w, k
-    HI, dI = 64, 128
     q = torch.randn(B, 1, HI, dI, generator=g).to(torch.bfloat16)
     w = torch.rand(B, 1, HI, generator=g)
     k = torch.randn(B, L, dI, generator=g).to(torch.bfloat16)
@@ -96,6 +95,22 @@ def test_decode_select_equals_oracle_topk_of_the_same_scores(kind, B, L, topk, k
     q, w, k = _index_inputs(kind, B, L, seed=B * 1000 + L % 997)
     kv_len = None if kv is None else torch.tensor(kv, dtype=torch.int32)
     _check_decode(q, w, k, None, kv_len, topk)
+
+
+@pytest.mark.parametrize("HI,dI", [(16, 128), (32, 128), (128, 128), (64, 64)])
+def test_decode_select_other_indexer_shapes(HI, dI):
+    # every compiled score kernel leaves its lists the same way (the 128-head
+    # query block runs a four-deep key ring instead of eight)
+    _announce(f"decode select H^I={HI} d^I={dI} B=3 L=20000 k=1024")
+    q, w, k = _index_inputs("clustered", 3, 20000, seed=HI * 7 + dI, HI=HI, dI=dI)
+    kv_len = torch.tensor([20000, 12345, 900], dtype=torch.int32)
+    _check_decode(q, w, k, None, kv_len, 1024)
+
+
+def test_decode_select_fp8_keys_small_query_block():
+    _announce("decode select fp8 keys H^I=16 B=2 L=30000 k=2048")
+    wl = workloads.decode_128k_fp8(B=2, L=30000, HI=16)
+    _check_decode(wl.q_idx, wl.w, wl.k_idx, wl.k_scale, wl.kv_len, wl.topk)
 
 
 def test_decode_select_fp8_keys():
