@@ -662,9 +662,9 @@ __global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) 
 //     fitted to [lo0, max key]; after one barrier every wave finds tau's bin
 //     in it (wave_rank_bin) and, when the bin holds at most 64 keys, their
 //     holders gather them (one more barrier) and every wave ranks them.  A
-//     fuller bin takes radix passes over the kept keys (kept_tau).  When the lists are no valid
-//     source, or hold more keys than LDS does, the row's scores are read
-//     directly (row_select).
+//     fuller bin takes radix passes over the kept keys (kept_tau).  When the
+//     lists are no valid source, or hold more keys than LDS does, the row's
+//     scores are read directly (row_select).
 //  3. The selected positions are marked in two bitmaps of the row (keys >
 //     tau, keys == tau); a block scan of the bitmap words' counts in position
 //     order gives every selected position its ascending slot and every tie its
