@@ -113,6 +113,14 @@ def test_decode_select_fp8_keys_small_query_block():
     _check_decode(wl.q_idx, wl.w, wl.k_idx, wl.k_scale, wl.kv_len, wl.topk)
 
 
+def test_decode_beyond_the_lists_limit_takes_the_split_select():
+    # rows longer than 131072 positions: the score kernel leaves no lists and
+    # the chunked split select runs over the scores, with the same result rule
+    _announce("decode select L=140000 (split path) B=2 k=2048")
+    q, w, k = _index_inputs("spread", 2, 140000, seed=140)
+    _check_decode(q, w, k, None, torch.tensor([140000, 131100], dtype=torch.int32), 2048)
+
+
 def test_decode_select_fp8_keys():
     _announce("decode select fp8 keys B=3 L=40000 k=2048")
     wl = workloads.decode_128k_fp8(B=3, L=40000)
