@@ -126,6 +126,16 @@ def test_decode_validation(lib):
     assert f(*args, A, need - 256, None) == 6
 
 
+def test_decode_workspace_holds_scores_lists_and_partials(lib):
+    # decode, B=32, L=32768, k=2048, H=128: the fp32 score rows (4 bytes per
+    # position), the score kernel's candidate lists ((key, position) pairs, up
+    # to every position: 8 bytes), and the MLA's KV-split partials (4 splits x
+    # 128 heads x (512 + 2) floats per query)
+    B, L, k, H = 32, 32768, 2048, 128
+    need = lib.sparse_attn_workspace_bytes(2, B, 1, L, k, H, 512)
+    assert need >= B * L * (4 + 8) + B * H * 4 * 514 * 4
+
+
 def test_block_validation(lib):
     f = lib.sparse_attn_block_decode
     F = ctypes.c_float(0.1)
