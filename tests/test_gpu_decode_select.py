@@ -121,6 +121,45 @@ def test_decode_beyond_the_lists_limit_takes_the_split_select():
     _check_decode(q, w, k, None, torch.tensor([140000, 131100], dtype=torch.int32), 2048)
 
 
+def test_decode_select_never_takes_nan_scores():
+    # NaN index scores are never selected (documented: the library excludes
+    # non-finite index scores).  The ReLU maps a NaN product to 0, so NaN
+    # scores come from the fp8 path's per-token scale, which multiplies the
+    # finished score.  The oracle refuses non-finite scores, so the fused
+    # decode is checked against the staged top-k over the same scores, and
+    # against the oracle's top-k over the finite positions.
+    _announce("decode select with NaN scores B=3 L=32768 k=2048")
+    k = 2048
+    wl = workloads.decode_128k_fp8(B=3, L=32768)
+    B, L = wl.B, wl.L
+    g = torch.Generator().manual_seed(5)
+    nanpos = torch.randperm(L, generator=g)[:700]
+    scale = wl.k_scale.clone()
+    scale[:, nanpos] = float("nan")
+    qd, wd, kd, sd = wl.q_idx.to(DEV), wl.w.to(DEV), wl.k_idx.to(DEV), scale.to(DEV)
+    gm = torch.Generator(device=DEV).manual_seed(11)
+    q_lat = torch.randn(B, 1, H, DC, device=DEV, generator=gm).to(torch.bfloat16)
+    q_rope = torch.randn(B, 1, H, DR, device=DEV, generator=gm).to(torch.bfloat16)
+    kv = torch.randn(B, L, DC + DR, device=DEV, generator=gm).to(torch.bfloat16)
+    _, _, idx = api.sparse_attn_decode(qd, wd, kd, sd, None, k, q_lat, q_rope,
+                                       kv[..., :DC], kv[..., DC:], 0.04)
+    s = api.sparse_attn_indexer_scores(qd, wd, kd, k_scale=sd)
+    si, sc = api.sparse_attn_topk(s, k)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, si.cpu().numpy())
+    sn = s.cpu().double().numpy()
+    assert np.isnan(sn[:, 0, nanpos.numpy()]).all()  # the case is really exercised
+    for b in range(B):
+        sel = gi[b, 0][gi[b, 0] >= 0]
+        assert np.isfinite(sn[b, 0, sel]).all()
+        fin = np.nonzero(np.isfinite(sn[b, 0]))[0]
+        assert len(sel) == min(k, len(fin))
+        # the oracle on the finite positions only, mapped back to positions
+        oi, _ = oracle.topk(sn[b:b + 1, :, fin], k)
+        assert np.array_equal(np.sort(fin[oi[0, 0][oi[0, 0] >= 0]]), sel)
+
+
 def test_decode_select_fp8_keys():
     _announce("decode select fp8 keys B=3 L=40000 k=2048")
     wl = workloads.decode_128k_fp8(B=3, L=40000)
