@@ -252,14 +252,28 @@ __device__ __forceinline__ void kept_tau(const uint32_t (&rk)[RUN], int s, uint3
 
 // The row's selected positions straight from its scores (candidates: the V
 // positions < lim with a key): radix passes over all its keys find tau when
-// V > k, then the emission walks the row in position order, NT positions per
-// round, passing emit(slot, position).  Run by all NT threads.
+// V > k, then the emission walks the row in position order.  Both take the
+// row in rounds of kRsU * NT positions, each thread's kRsU loads in flight
+// together (position q0 + u NT + thread in round q0); the emission's slots
+// come from one scan per round over the (u, wave) totals, in that order.
+// Passes emit(slot, position).  Run by all NT threads.
+constexpr int kRsU = 8;
 template <int NT, class Emit>
 __device__ __forceinline__ void row_select(const float* srow, int k, int lim, int V,
                                            const SplitSmem& sm, Emit&& emit) {
-  const int tid = threadIdx.x;
+  constexpr int NWV = NT / 64, NTAB = kRsU * NWV;
+  static_assert(NTAB <= 64, "one wave scans the round's (u, wave) totals in sm.small");
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   int* const red = sm.red;
   int* const found = sm.found;
+  int* const tab = (int*)sm.small;  // [NTAB] (u, wave) prefixes, [64] the round's total
+  auto load = [&](int q0, uint32_t (&c)[kRsU]) {
+    float f[kRsU];
+#pragma unroll
+    for (int u = 0; u < kRsU; ++u) f[u] = srow[min(q0 + u * NT + tid, lim - 1)];
+#pragma unroll
+    for (int u = 0; u < kRsU; ++u) c[u] = q0 + u * NT + tid < lim ? score_key(f[u]) : 0u;
+  };
   // ---- straight from the row: radix passes over all its keys ----
   uint32_t tau = 0u;  // V <= k: every candidate (key > 0) is taken
   int need_eq = 0;
@@ -274,10 +288,12 @@ __device__ __forceinline__ void row_select(const float* srow, int k, int lim, in
       for (int i = tid; i < kSpBins; i += NT) sm.hist[i] = 0;
       __syncthreads();
 #pragma unroll 1
-      for (int q0 = 0; q0 < lim; q0 += NT) {
-        const int q = q0 + tid;
-        const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
-        hist_add(sm.hist, (c >> s2) & dmask, c != 0u && (c & pmask) == prefix);
+      for (int q0 = 0; q0 < lim; q0 += kRsU * NT) {
+        uint32_t c[kRsU];
+        load(q0, c);
+#pragma unroll
+        for (int u = 0; u < kRsU; ++u)
+          hist_add(sm.hist, (c[u] >> s2) & dmask, c[u] != 0u && (c[u] & pmask) == prefix);
       }
       sp_rank_bin<NT>(sm.hist, krem, red, found);
       prefix |= (uint32_t)found[0] << s2;
@@ -287,17 +303,39 @@ __device__ __forceinline__ void row_select(const float* srow, int k, int lim, in
     tau = prefix;
     need_eq = krem;
   }
-  // emission in position order, NT positions per round
+  // ---- emission in position order ----
   int run_gt = 0, run_eq = 0;
 #pragma unroll 1
-  for (int q0 = 0; q0 < lim; q0 += NT) {
-    const int q = q0 + tid;
-    const uint32_t c = q < lim ? score_key(srow[q]) : 0u;
-    const int g = c != 0u && c > tau, eq = c != 0u && c == tau;
-    int total;
-    const int before = sp_scan_excl<NT>((g << 16) | eq, red, total);
-    const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
-    if (g || (eq && eqb < need_eq)) emit(gtb + min(eqb, need_eq), q);
+  for (int q0 = 0; q0 < lim; q0 += kRsU * NT) {
+    uint32_t c[kRsU];
+    load(q0, c);
+    int cu[kRsU], wi[kRsU];  // (keys > tau) << 16 | ties: at most kRsU * NT each
+#pragma unroll
+    for (int u = 0; u < kRsU; ++u) {
+      cu[u] = ((c[u] != 0u && c[u] > tau) << 16) | (c[u] != 0u && c[u] == tau);
+      wi[u] = wave_scan_incl(cu[u]);
+    }
+    __syncthreads();  // the previous round's table is read
+    if (lane == 63) {
+#pragma unroll
+      for (int u = 0; u < kRsU; ++u) tab[u * NWV + wave] = wi[u];
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefixes in (u, wave) order: position order
+      const int v = lane < NTAB ? tab[lane] : 0;
+      const int inc = wave_scan_incl(v);
+      if (lane < NTAB) tab[lane] = inc - v;
+      if (lane == 63) tab[64] = inc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRsU; ++u) {
+      const int before = tab[u * NWV + wave] + wi[u] - cu[u];
+      const int gtb = run_gt + (before >> 16), eqb = run_eq + (before & 0xffff);
+      const bool g = (cu[u] >> 16) != 0, eq = (cu[u] & 1) != 0;
+      if (g || (eq && eqb < need_eq)) emit(gtb + min(eqb, need_eq), q0 + u * NT + tid);
+    }
+    const int total = tab[64];
     run_gt += total >> 16;
     run_eq += total & 0xffff;
   }

@@ -662,9 +662,15 @@ __global__ __launch_bounds__(NT) void topk_split_select_kernel(TopkSplitArgs a) 
 //     fitted to [lo0, max key]; after one barrier every wave finds tau's bin
 //     in it (wave_rank_bin) and, when the bin holds at most 64 keys, their
 //     holders gather them (one more barrier) and every wave ranks them.  A
-//     fuller bin takes radix passes over the kept keys (kept_tau).  When the
-//     lists are no valid source, or hold more keys than LDS does, the row's
-//     scores are read directly (row_select).
+//     fuller bin takes radix passes over the kept keys (kept_tau).
+//  2b. When fewer than k kept keys are >= lo0 (a list held more of the top k
+//     than its floor kept), t = the floor of the histogram bin that holds the
+//     k-th largest kept key is a lower bound of tau (the k-th largest of a
+//     subset is no larger).  Every list that dropped keys >= t reads its
+//     positions' scores back and appends those keys; the kept keys >= t are
+//     then all of the row's, at least k of them, and kept_tau ranks them.
+//     When the lists hold more keys than LDS does, or fewer than k in all,
+//     the row's scores are read directly (row_select).
 //  3. The selected positions are marked in two bitmaps of the row (keys >
 //     tau, keys == tau); a block scan of the bitmap words' counts in position
 //     order gives every selected position its ascending slot and every tie its
@@ -674,6 +680,7 @@ constexpr int kKpThreads = 512;
 constexpr int kKpKeep = 12288;  // kept keys held in LDS
 constexpr int kKpSpec = 12;     // entries per thread in the first round of loads
 constexpr int kKpWords = kKeepMaxL / 32;
+constexpr int kKpRescan = 8;    // score loads per thread in flight when lists read back
 static_assert(kKpWords % kKpThreads == 0 && kKpKeep < 65536 && kTopkMaxK < 65536,
               "bitmap words per thread; packed counts");
 
@@ -699,6 +706,8 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
   __shared__ uint32_t wlo[NWV], whi[NWV], wmx[NWV];
   __shared__ __align__(16) uint32_t small[68];  // 64 keys read 16 bytes at a time, + 2 results
   __shared__ int nsmall;
+  __shared__ int nres, ndef, defl[kKpThreads];  // lists read back: count and ids
+  __shared__ uint32_t deflo[kKpThreads];        // and their floors
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int lim = candidate_limit(nullptr, a.kv_len, (int)row, row, a.L);
@@ -757,6 +766,8 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
   bool fast = V > k ? K >= k && K <= kKpKeep : K == V;
   uint32_t tau = 0u;  // V <= k: every kept key (>= 1) is above it
   int need_eq = 0;
+  bool reread = false;  // tau comes from the lists with keys read back (2b)
+  int Kt = K;           // kept keys in LDS, read-back keys included
   if (fast) {
     const uint32_t lo0 = max(lomax, lomin);
     const int sh = max(0, 32 - __clz(kmax - lo0) - 11);  // (range >> sh) < 2048
@@ -784,6 +795,7 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
       int bin, above, C;
       wave_rank_bin(hist, k, bin, above, C);
       fast = C >= k;  // uniform: the same histogram in every wave
+      reread = !fast;
       if (fast && hist[bin] <= 64) {
         // the keys of tau's bin: their holders append them to `small` (one
         // LDS atomic per wave), then every wave ranks them against each other
@@ -837,20 +849,97 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
         kept_tau<NT>(rk, s, lo0, kmax, k, sm, tau, need_eq);
       }
     }
-    if (fast) {
-      // ---- 3. bitmaps (each team marks its own entries), then slots ----
+    if (reread) {
+      // ---- 2b. t from a histogram of all kept keys, then the lists read back ----
+      const int sh2 = max(0, 32 - __clz(kmax - lomin) - 11);  // (range >> sh2) < 2048
+      __syncthreads();  // every wave has read the histogram
+      for (int i = tid; i < kSpBins; i += NT) hist[i] = 0;
+      if (tid == 0) nres = ndef = 0;
+      __syncthreads();
+      for (int i = tid; i < K; i += NT) atomicAdd(&hist[(kk[i] - lomin) >> sh2], 1);
+      __syncthreads();
+      int bin, above, C;
+      wave_rank_bin(hist, k, bin, above, C);  // k <= K: the bin exists
+      const uint32_t t = lomin + ((uint32_t)bin << sh2);
+      if (lead && nj < inf.y && (uint32_t)inf.z > t) {  // dropped keys >= t
+        const int d = atomicAdd(&ndef, 1);
+        defl[d] = j;
+        deflo[d] = (uint32_t)inf.z;
+      }
+      __syncthreads();
+      // list jj's positions: the 64-position runs 64 (jj + nwg c) + [0, 64)
+      // (the score kernel's dealing of chunks); its slot q is position
+      // 64 (jj + nwg (q / 64)) + q % 64.  Keys in [t, floor) are appended.
+      const float* srow = a.scores + row * a.L;
+      const int slots = ndef * cap;
+      for (int g0 = 0; g0 < slots; g0 += NT * kKpRescan) {
+        float f[kKpRescan];
+        int pp[kKpRescan];
+        uint32_t fl[kKpRescan];
 #pragma unroll
-      for (int m = 0; m < kKpSpec; ++m) {
-        const int i = r + tpw * m;
-        if (member && i < nj && ent[m].x >= tau) {
-          const int p = (int)ent[m].y;
-          atomicOr(ent[m].x > tau ? &gtm[p >> 5] : &eqm[p >> 5], 1u << (p & 31));
+        for (int u = 0; u < kKpRescan; ++u) {
+          const int g = g0 + u * NT + tid;
+          const int di = g < slots ? g / cap : 0;
+          const int q = g - di * cap, jj = defl[di];
+          const int p = 64 * (jj + nwg * (q >> 6)) + (q & 63);
+          const bool ok = g < slots && p < lim;
+          pp[u] = ok ? p : -1;
+          fl[u] = deflo[di];
+          f[u] = srow[ok ? p : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kKpRescan; ++u) {
+          const uint32_t x = pp[u] >= 0 ? score_key(f[u]) : 0u;
+          const bool take = x != 0u && x >= t && x < fl[u];
+          const uint64_t m = __ballot(take);
+          if (m == 0) continue;  // uniform
+          const int first = __ffsll((unsigned long long)m) - 1;
+          int base = 0;
+          if (lane == first) base = atomicAdd(&nres, __popcll(m));
+          const int slot = K + __builtin_amdgcn_readlane(base, first) + mbcnt(m);
+          if (take && slot < kKpKeep) {
+            kk[slot] = x;
+            kpos[slot] = pp[u];
+          }
         }
       }
-      if (member) {
-        for (int i = r + tpw * kKpSpec; i < nj; i += tpw) {
-          const uint32_t x = kk[d0 + i];
-          const int p = kpos[d0 + i];
+      __syncthreads();
+      Kt = K + nres;
+      fast = Kt <= kKpKeep;  // uniform
+      if (fast) {
+        const int s = (Kt + NT - 1) / NT;  // <= kRun
+        const int j0 = tid * s;
+        uint32_t rk[kRun];
+#pragma unroll
+        for (int e = 0; e < kRun; ++e) {
+          if (e >= s) break;  // uniform
+          rk[e] = j0 + e < Kt ? kk[j0 + e] : 0u;
+        }
+        kept_tau<NT>(rk, s, t, kmax, k, sm, tau, need_eq);  // the keys >= t: >= k of them
+      }
+    }
+    if (fast) {
+      // ---- 3. bitmaps (each team marks its own entries), then slots ----
+      if (!reread) {
+#pragma unroll
+        for (int m = 0; m < kKpSpec; ++m) {
+          const int i = r + tpw * m;
+          if (member && i < nj && ent[m].x >= tau) {
+            const int p = (int)ent[m].y;
+            atomicOr(ent[m].x > tau ? &gtm[p >> 5] : &eqm[p >> 5], 1u << (p & 31));
+          }
+        }
+        if (member) {
+          for (int i = r + tpw * kKpSpec; i < nj; i += tpw) {
+            const uint32_t x = kk[d0 + i];
+            const int p = kpos[d0 + i];
+            if (x >= tau) atomicOr(x > tau ? &gtm[p >> 5] : &eqm[p >> 5], 1u << (p & 31));
+          }
+        }
+      } else {
+        for (int i = tid; i < Kt; i += NT) {
+          const uint32_t x = kk[i];
+          const int p = kpos[i];
           if (x >= tau) atomicOr(x > tau ? &gtm[p >> 5] : &eqm[p >> 5], 1u << (p & 31));
         }
       }
@@ -867,7 +956,7 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
         ew[i] = wd < NW ? eqm[wd] : 0u;
         c += (__popc(gw[i]) << 16) + __popc(ew[i]);
       }
-      // keys > tau < k and ties <= K: 16 bits each
+      // keys > tau < k and ties <= Kt: 16 bits each
       const int ci = wave_scan_incl(c);
       if (lane == 63) wt[wave] = ci;
       __syncthreads();
