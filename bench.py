@@ -22,7 +22,7 @@ The JSON line carries, besides the contract fields:
 Usage: python bench.py [--steps K] [--warmup W]
        [--workload decode_32k|decode_128k_fp8|prefill_16k|block_sparse_64k|csa_decode|
                    prefill_crossover]
-       [--staged] [--shared-choice] [--no-cpu-baseline] [--kernel-only]
+       [--staged] [--fused-select] [--shared-choice] [--no-cpu-baseline] [--kernel-only]
 """
 import argparse
 import json
@@ -355,10 +355,13 @@ def prefill_mla_flop(wl, rows):
 
 
 def run_prefill(args, api, dev):
-    """Causal prefill, T = L = 16384, through sparse_attn_prefill (sparse mode):
-    the fused select (indexer scores and Top-K per query row, the row held on
-    chip, no [T, L] score tensor), then the sparse MLA for every query.
-    --staged times the three-call path instead (score tensor, top-k, MLA)."""
+    """Causal prefill, T = L = 16384, through sparse_attn_prefill (sparse mode).
+    At this size the entry point selects staged (the indexer scores of all T
+    rows into its workspace, then the top-k), then runs the sparse MLA for
+    every query; the roofline times that select as the same two calls.
+    --staged times the three-call path (score tensor, top-k, MLA);
+    --fused-select times the fused select (indexer scores and Top-K per query
+    row, the row held on chip, no [T, L] score tensor) and the MLA."""
     import torch
     from top_indexer_sparse_amd import workloads
     log("generating prefill_16k")
@@ -371,12 +374,25 @@ def run_prefill(args, api, dev):
     out = torch.empty((1, T, wl.H, wl.dc), dtype=torch.float32, device=dev)
     lse = torch.empty((1, T, wl.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    if args.staged:
+    mws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_MLA_FORWARD, 1, T, L, k,
+                                                              wl.H, wl.dc)),
+                      dtype=torch.uint8, device=dev)
+
+    def mla():
+        api.sparse_attn_mla_forward(t.q_lat, t.q_rope, c_kv, k_rope, idx, wl.sm_scale,
+                                    out=out, lse=lse, ws=mws, stream=stream)
+
+    if args.fused_select:
+        def select():
+            api.sparse_attn_prefill_select(t.q_idx, t.w, t.k_idx, k, q_pos=t.q_pos, idx=idx,
+                                           count=cnt, stream=stream)
+
+        def step():
+            select()
+            mla()
+    else:
         scores = torch.empty((1, T, L), dtype=torch.float32, device=dev)
         tws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_TOPK, 1, T, L, k, 0, 0)),
-                          dtype=torch.uint8, device=dev)
-        mws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_MLA_FORWARD, 1, T, L, k,
-                                                                  wl.H, wl.dc)),
                           dtype=torch.uint8, device=dev)
 
         def select():
@@ -385,23 +401,20 @@ def run_prefill(args, api, dev):
             api.sparse_attn_topk(scores, k, q_pos=t.q_pos, idx=idx, count=cnt, ws=tws,
                                  stream=stream)
 
-        def step():
-            select()
-            api.sparse_attn_mla_forward(t.q_lat, t.q_rope, c_kv, k_rope, idx, wl.sm_scale,
-                                        out=out, lse=lse, ws=mws, stream=stream)
-    else:
-        ws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_PREFILL, 1, T, L, k,
-                                                                 wl.H, wl.dc)),
-                         dtype=torch.uint8, device=dev)
+        if args.staged:
+            def step():
+                select()
+                mla()
+        else:
+            ws = torch.empty(max(1, api.sparse_attn_workspace_bytes(api.SA_OP_PREFILL, 1, T, L, k,
+                                                                     wl.H, wl.dc)),
+                             dtype=torch.uint8, device=dev)
 
-        def select():
-            api.sparse_attn_prefill_select(t.q_idx, t.w, t.k_idx, k, q_pos=t.q_pos, idx=idx,
-                                           count=cnt, stream=stream)
-
-        def step():
-            api.sparse_attn_prefill(t.q_idx, t.w, t.k_idx, k, t.q_lat, t.q_rope, c_kv, k_rope,
-                                    wl.sm_scale, q_pos=t.q_pos, mode=api.SA_PREFILL_SPARSE,
-                                    out=out, lse=lse, idx_out=idx, ws=ws, stream=stream)
+            def step():
+                api.sparse_attn_prefill(t.q_idx, t.w, t.k_idx, k, t.q_lat, t.q_rope, c_kv,
+                                        k_rope, wl.sm_scale, q_pos=t.q_pos,
+                                        mode=api.SA_PREFILL_SPARSE, out=out, lse=lse,
+                                        idx_out=idx, ws=ws, stream=stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -410,13 +423,14 @@ def run_prefill(args, api, dev):
     log(f"timing {args.steps} steps")
     ms = time_events(step, args.steps, stream)
     qps = T / (ms * 1e-3)
-    log(f"{ms:.2f} ms/step, {qps:,.0f} queries/s ({'staged' if args.staged else 'fused select'})")
+    path = "fused_select" if args.fused_select else "staged" if args.staged else "sparse_attn_prefill"
+    log(f"{ms:.2f} ms/step, {qps:,.0f} queries/s ({path})")
     if args.kernel_only:
         return None
     sel_ms = timed_after(step, select, max(3, min(args.steps, 10)), stream)
     flop = prefill_indexer_flop(wl)
     tfs = flop / (sel_ms * 1e-3) / 1e12
-    what = "indexer scores + top-k" if args.staged else "fused select (scores + top-k)"
+    what = "fused select (scores + top-k)" if args.fused_select else "indexer scores + top-k"
     log(f"{what} {sel_ms:.3f} ms: indexer flops at {tfs:,.0f} TFLOP/s = "
         f"{100 * tfs / BF16_PEAK_TFLOPS:.1f}% of bf16 MFMA peak")
     rows = int(torch.clamp(cnt, max=k).sum().item())
@@ -438,7 +452,7 @@ def run_prefill(args, api, dev):
         "data": "synthetic",
         "config": {"workload": wl.name, "B": 1, "T": T, "L": L, "topk": k, "HI": wl.HI,
                    "dI": wl.dI, "H": wl.H, "dc": wl.dc, "dR": wl.dR,
-                   "path": "staged" if args.staged else "fused_select"},
+                   "path": path},
         "roofline": {"bound": "mfma", "kernel": what, "achieved": round(tfs, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -725,7 +739,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--staged", action="store_true",
                     help="prefill_16k: time the three-call path (score tensor, top-k, MLA) "
-                         "instead of the fused select")
+                         "instead of sparse_attn_prefill")
+    ap.add_argument("--fused-select", action="store_true",
+                    help="prefill_16k: time the fused select (no score tensor) and the MLA "
+                         "instead of sparse_attn_prefill")
     ap.add_argument("--shared-choice", action="store_true",
                     help="block_sparse_64k: one block choice per KV group (sum of its heads' "
                          "block scores)")

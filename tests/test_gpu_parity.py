@@ -85,6 +85,41 @@ def test_indexer_mfma_prefill(fp8):
     assert_scores_close(g, ref, fl)
 
 
+@pytest.mark.parametrize("T", [1, 16])
+def test_indexer_mfma_relu_maps_nan_products_to_zero(T):
+    # The MFMA score kernels take ReLU(x) as the median of x, 0 and +inf:
+    # a NaN head product contributes 0, as fmaxf(x, 0) would.  A key row
+    # with NaN elements then scores exactly 0, and every other position
+    # scores what it scores with that row zeroed (the oracle's input, which
+    # must be finite).  T = 1 runs the decode kernel, T = 16 with q_pos the
+    # staged prefill kernel and the fused prefill select.
+    _announce(f"indexer NaN key rows T={T}")
+    g0 = torch.Generator().manual_seed(41)
+    B, HI, dI, L = 2, 64, 128, 700
+    q = torch.randn(B, T, HI, dI, generator=g0).to(torch.bfloat16)
+    w = torch.rand(B, T, HI, generator=g0) - 0.2
+    k = torch.randn(B, L, dI, generator=g0).to(torch.bfloat16)
+    bad = [3, 64, 65, 333, 683]  # candidates of every query (q_pos >= L - T)
+    k_nan = k.clone()
+    k_nan[0, bad] = float("nan")
+    k_nan[1, bad, 7] = float("nan")  # one NaN element per row
+    k_zero = k.clone()
+    k_zero[:, bad] = 0
+    qp = None if T == 1 else torch.arange(L - T, L, dtype=torch.int32).repeat(B, 1)
+    gq, gw, gk, gqp = _cuda(q, w, k_nan, qp)
+    g = api.sparse_attn_indexer_scores(gq, gw, gk, q_pos=gqp)
+    torch.cuda.synchronize()
+    gs = g.cpu()
+    assert (gs[:, :, bad] == 0).all().item()
+    ref = oracle.indexer(q, w, k_zero, q_pos=qp)
+    assert_scores_close(g, ref, score_floor(q, w, oracle.decode(k_zero)))
+    if T > 1:  # the fused select scores with the same arithmetic
+        idx, cnt = api.sparse_attn_prefill_select(gq, gw, gk, 64, q_pos=gqp)
+        torch.cuda.synchronize()
+        oi, oc = oracle.topk(gs.double().numpy(), 64, q_pos=qp)
+        assert np.array_equal(idx.cpu().numpy(), oi)
+
+
 def test_indexer_vector_path_bf16_odd_heads():
     _announce("indexer vector path HI=12 bf16")
     g0 = torch.Generator().manual_seed(5)

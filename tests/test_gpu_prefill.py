@@ -284,11 +284,17 @@ def test_prefill_dense_fullsize_sampled():
     assert_attention_close(out[:, rows], ro, ATTN_ATOL_BF16, lse[:, rows], rl)
 
 
-def test_prefill_sparse_long_rows_chunked():
-    # rows above the fused select's 32768 positions take the staged select in
-    # chunks of 4096 query rows per sequence: 2 sequences x (4096 + 104) rows
-    _announce("prefill sparse L=33000 T=4200 B=2 (chunked select)")
-    wl = workloads.prefill_batch(B=2, T=4200, L=33000, HI=64, dI=128, topk=2048, H=64)
+@pytest.mark.parametrize("B,T,L", [
+    # rows above the fused select's 32768 positions: staged, in chunks of as
+    # many query rows as 1 GiB of scores holds (4096 at L = 65536), so each
+    # sequence runs 4096 + 104 rows
+    (2, 4200, 65536),
+    # T >= 2048 with L >= 16384: staged (faster there), one chunk of T rows
+    (1, 2100, 20000),
+])
+def test_prefill_sparse_staged_select(B, T, L):
+    _announce(f"prefill sparse B={B} T={T} L={L} (staged select)")
+    wl = workloads.prefill_batch(B=B, T=T, L=L, HI=64, dI=128, topk=2048, H=64)
     t = wl.to(DEV)
     idx = torch.empty((wl.B, wl.T, wl.topk), dtype=torch.int32, device=DEV)
     out, lse = _prefill(t, wl, api.SA_PREFILL_SPARSE, idx_out=idx)
@@ -297,7 +303,7 @@ def test_prefill_sparse_long_rows_chunked():
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
     assert np.array_equal(gi, si.cpu().numpy())
-    rows = [0, 4095, 4096, 4199]
+    rows = sorted({0, min(4095, T - 1), min(4096, T - 1), T - 1})
     sr = s[:, rows].cpu().double().numpy()
     oi, oc = oracle.topk(sr, wl.topk, q_pos=wl.q_pos[:, rows].contiguous())
     assert np.array_equal(gi[:, rows], oi)

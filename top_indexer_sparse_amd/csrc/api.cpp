@@ -139,14 +139,32 @@ int index_and_select(sa::IndexerArgs ia, const sa::TopkArgs& ta, void* topk_ws, 
   return hip_status(sa::launch_topk(ta, st), "decode topk launch");
 }
 
-// Rows longer than the fused select's on-chip row take the staged select in
-// chunks of this many query rows: a [chunk, L] score buffer instead of
-// [B, T, L], and enough rows per chunk (512 score work-groups) to fill the GPU.
+// The prefill select runs staged (stage 1 into a score buffer, then stage 2)
+// where that is faster than the fused select, and wherever rows are longer
+// than the fused select holds on chip.  Measured on MI355X (k = 2048, H^I =
+// 64, d^I = 128, bf16, the last T queries of an L-token context): staged
+// 1.08 ms against 1.17 fused at T = 4096, L = 16384, and 1.10 against 2.18
+// at T = 2048, L = 32768 (the fused select keeps one row per work-group
+// there); the fused select is faster with fewer query rows (0.35 against
+// 0.51 ms at T = 1024, L = 16384) or shorter rows (0.29 against 0.37 at
+// T = L = 4096).
+constexpr int kPrefillStagedMinRows = 2048;
+constexpr int kPrefillStagedMinL = 16384;
+// Staged chunks of query rows per sequence: as many as a 1 GiB score buffer
+// holds, at least 4096 (512 score work-groups, enough to fill the GPU), at
+// most T.  One chunk keeps the score kernel's heaviest-rows-first order over
+// the whole sequence.
+constexpr size_t kPrefillScoreBudget = 1ull << 30;
 constexpr int kPrefillChunkRows = 4096;
+bool prefill_staged(int T, int L, int k) {
+  return T > 0 && (L > sa::kPrefillSelectMaxL ||
+                   (T >= kPrefillStagedMinRows && L >= kPrefillStagedMinL &&
+                    sa::topk_supported(L, k)));
+}
 
 // prefill workspace layout: idx [B, T, k] | count [B, T] | mla ws (the larger
-// of the sparse and the dense attention's) | for L above the fused select's
-// limit: chunk scores [chunk, L] | top-k ws of one chunk
+// of the sparse and the dense attention's) | when the select runs staged:
+// chunk scores [chunk, L] | top-k ws of one chunk
 struct PrefillWs {
   size_t idx, count, mla, scores, topk, total;
   int chunk;  // query rows per staged chunk (0: the fused select runs)
@@ -164,8 +182,10 @@ PrefillWs prefill_ws(int B, int T, int L, int k, int H, int dc) {
   off = align256(off + (ms > md ? ms : md));
   w.chunk = 0;
   w.scores = w.topk = off;
-  if (L > sa::kPrefillSelectMaxL && T > 0) {
-    w.chunk = T < kPrefillChunkRows ? T : kPrefillChunkRows;
+  if (prefill_staged(T, L, k)) {
+    const int64_t fit = (int64_t)(kPrefillScoreBudget / ((size_t)L * sizeof(float)));
+    const int64_t rows = fit > kPrefillChunkRows ? fit : kPrefillChunkRows;
+    w.chunk = T < rows ? T : (int)rows;
     off = align256(off + (size_t)w.chunk * L * sizeof(float));
     w.topk = off;
     off = align256(off + sa::topk_workspace_bytes(1, w.chunk, L, k < 1 ? 1 : k));
@@ -174,15 +194,15 @@ PrefillWs prefill_ws(int B, int T, int L, int k, int H, int dc) {
   return w;
 }
 
-// allow_long: rows above the fused select's limit are accepted (the prefill
-// entry point then selects through chunked score buffers)
-int check_prefill_select(const sa::IndexerArgs& a, int k, bool allow_long = false) {
+// staged: the prefill entry point selects through chunked score buffers, so
+// rows above the fused select's limit are accepted
+int check_prefill_select(const sa::IndexerArgs& a, int k, bool staged = false) {
   int s = check_indexer(a);
   if (s != SA_OK) return s;
   REQUIRE(k >= 1, SA_ERR_SHAPE, "prefill_select: k=%d must be >= 1", k);
   REQUIRE(a.L >= 1, SA_ERR_SHAPE, "prefill_select: L=%d must be >= 1", a.L);
   REQUIRE(sa::prefill_select_supported(a, k) ||
-              (allow_long && a.L > sa::kPrefillSelectMaxL && sa::indexer_uses_mfma(a)),
+              (staged && sa::indexer_uses_mfma(a)),
           SA_ERR_UNSUPPORTED,
           "prefill_select: (q_dtype=%d, k_dtype=%d, HI=%d, dI=%d, L=%d) outside the compiled set "
           "(bf16 queries, bf16/fp8 keys, HI in {16,32,64,128}, dI in {64,128}, L <= %d)",
@@ -358,7 +378,7 @@ int sparse_attn_prefill(const void* q_idx, int q_idx_dtype, const float* w, cons
     ma.dense_q_pos = q_pos;
     ma.dense_kv_len = kv_len;
   }
-  int s = dense ? SA_OK : check_prefill_select(ia, k, true);
+  int s = dense ? SA_OK : check_prefill_select(ia, k, lay.chunk > 0);
   if (s == SA_OK && !dense && lay.chunk > 0) {
     REQUIRE(sa::topk_supported(L, k), SA_ERR_UNSUPPORTED,
             "prefill: k=%d, L=%d outside the top-k set", k, L);

@@ -20,6 +20,22 @@ __device__ __forceinline__ int kmap(int ks, int g) {
   return FP8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
 }
 
+// ReLU of a contraction result in one VALU instruction, v_med3_f32(x, 0,
+// +inf): max(x, 0) for every x that is not NaN, and 0 for a NaN (an MFMA
+// result is a quiet NaN, and a median with a NaN operand is the smaller of
+// the other two) -- what fmaxf(x, 0) gives.  fmaxf takes two instructions,
+// the first quieting a signaling NaN that the compiler cannot rule out.  The
+// bound is +inf in a scalar register (`inf` from inf_sgpr()): as a constant
+// the compiler folds the median back into fmaxf.
+__device__ __forceinline__ float inf_sgpr() {
+  float v;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(v));
+  return v;
+}
+__device__ __forceinline__ float relu_acc(float x, float inf) {
+  return __builtin_amdgcn_fmed3f(x, 0.f, inf);
+}
+
 // Registers of one 16-position key chunk: KS bf16x8 B operands.
 template <int DI, bool FP8>
 struct KeyChunk {
@@ -80,14 +96,25 @@ struct QueryRegs {
     bf16x8 kb[KS];  // widened once, shared by every head tile
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kb[ks] = kc.operand(ks);
+    const float inf = inf_sgpr();
+    // head tiles in pairs, k-steps inside: the pair's products are
+    // independent, so they issue back to back instead of waiting on one
+    // accumulator chain
     float part = 0.f;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int h0 = 0; h0 < HT; h0 += 2) {
+      constexpr int NP = HT >= 2 ? 2 : 1;
+      floatx4 acc[NP];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ht][ks], kb[ks], acc);
+      for (int j = 0; j < NP; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part = fmaf(wr[ht][r], fmaxf(acc[r], 0.f), part);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < NP; ++j) acc[j] = mfma16x16x32(a[h0 + j][ks], kb[ks], acc[j]);
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part = fmaf(wr[h0 + j][r], relu_acc(acc[j][r], inf), part);
     }
     return sum_over_lane_groups_vx(part);  // callers run it with the whole wave
   }
@@ -105,6 +132,7 @@ __device__ __forceinline__ void score_pair(const QueryRegs<HT, DI, FP8>& q0,
   bf16x8 kb[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kb[ks] = kc.operand(ks);
+  const float inf = inf_sgpr();
   float p0 = 0.f, p1 = 0.f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -115,9 +143,9 @@ __device__ __forceinline__ void score_pair(const QueryRegs<HT, DI, FP8>& q0,
       a1 = mfma16x16x32(q1.a[ht][ks], kb[ks], a1);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p0 = fmaf(q0.wr[ht][r], fmaxf(a0[r], 0.f), p0);
+    for (int r = 0; r < 4; ++r) p0 = fmaf(q0.wr[ht][r], relu_acc(a0[r], inf), p0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p1 = fmaf(q1.wr[ht][r], fmaxf(a1[r], 0.f), p1);
+    for (int r = 0; r < 4; ++r) p1 = fmaf(q1.wr[ht][r], relu_acc(a1[r], inf), p1);
   }
   s0 = sum_over_lane_groups_vx(p0);
   s1 = sum_over_lane_groups_vx(p1);

@@ -324,39 +324,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(HT <= 4 ? 4
   const uint8_t* kb = k + (int64_t)b * L * ROWB;
   const float* scb = kscale ? kscale + (int64_t)b * L : nullptr;
 
-  // staging: each thread moves chunk ids tid, tid + 512, ... of a tile
-  constexpr int PER = (CPT + 511) / 512;
-  uintx4 stage[PER];
-  auto gload = [&](int tl) {
+  // staging: global->LDS copies, no registers in between.  Copy i of wave w
+  // fills the tile's 1 KB block w + 8 i: lane l writes 16-byte slot 64 blk + l
+  // (row r = slot / CPR, stored piece slot % CPR), so it reads piece
+  // (slot % CPR) ^ (r % CPR) of key row r, clamped to the last candidate.
+  constexpr int NBLK = CPT / 64;
+  constexpr int PERW = (NBLK + kPfWaves - 1) / kPfWaves;
+  const uint32_t lds_t = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tile[0][0];
+  const uint32_t lds_s = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&tscale[0][0];
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // in a scalar register
+  auto gcopy = [&](int buf, int tl) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + 512 * i;
-      if (c < CPT) {
-        const int r = c / CPR, o = c % CPR;
-        const int s = min(tl * kPfTile + r, lim_max - 1);
-        stage[i] = *(const uintx4*)(kb + (int64_t)s * ROWB + 16 * o);
+    for (int i = 0; i < PERW; ++i) {
+      const int blk = wave_s + kPfWaves * i;
+      if (blk < NBLK) {  // uniform over the wave
+        const int slot = 64 * blk + lane;
+        const int r = slot / CPR, o = (slot % CPR) ^ (r & (CPR - 1));
+        const int sr = min(tl * kPfTile + r, lim_max - 1);
+        dma16_addr(kb + (int64_t)sr * ROWB + 16 * o,
+                   lds_t + (uint32_t)(buf * kPfTile * LROW + 1024 * blk));
       }
     }
-  };
-  auto lstore = [&](int buf, int tl) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + 512 * i;
-      if (c < CPT) {
-        const int r = c / CPR, o = c % CPR;
-        *(uintx4*)(&tile[buf][r * LROW + 16 * (o ^ (r & (CPR - 1)))]) = stage[i];
-      }
-    }
-    if (scb && threadIdx.x < kPfTile)
-      tscale[buf][threadIdx.x] = scb[min(tl * kPfTile + (int)threadIdx.x, lim_max - 1)];
+    if (scb && wave_s == kPfWaves - 1)
+      dma4(uniform_ptr((const uint8_t*)scb), 4u * (uint32_t)min(tl * kPfTile + lane, lim_max - 1),
+           lds_s + (uint32_t)(4 * kPfTile * buf));
   };
 
-  gload(0);
-  lstore(0, 0);
-  __syncthreads();
+  gcopy(0, 0);
+  wait_vmcnt<0>();
+  lds_barrier();
   for (int tl = 0; tl < ntiles; ++tl) {
     const int buf = tl & 1;
-    if (tl + 1 < ntiles) gload(tl + 1);
+    // the other buffer was last read before the previous barrier
+    if (tl + 1 < ntiles) gcopy(buf ^ 1, tl + 1);
     const int base = tl * kPfTile;
     if (active && base < lim) {
 #pragma unroll
@@ -373,8 +373,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(HT <= 4 ? 4
         }
       }
     }
-    if (tl + 1 < ntiles) lstore(buf ^ 1, tl + 1);
-    __syncthreads();
+    wait_vmcnt<0>();  // this wave's copies of the next tile landed
+    lds_barrier();    // every wave's copies landed; this tile's reads are done
   }
 }
 
