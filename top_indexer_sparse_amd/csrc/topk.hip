@@ -849,7 +849,7 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
         kept_tau<NT>(rk, s, lo0, kmax, k, sm, tau, need_eq);
       }
     }
-    if (reread) {
+    if (__builtin_expect(reread, 0)) {
       // ---- 2b. t from a histogram of all kept keys, then the lists read back ----
       const int sh2 = max(0, 32 - __clz(kmax - lomin) - 11);  // (range >> sh2) < 2048
       __syncthreads();  // every wave has read the histogram
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(kKpThreads) void topk_keep_select_kernel(KeepSelArg
       }
     }
   }
-  if (!fast)
+  if (__builtin_expect(!fast, 0))
     row_select<NT>(a.scores + row * a.L, k, lim, V, sm, [&](int slot, int pos) { out[slot] = pos; });
   for (int i = n_sel + tid; i < k; i += NT) out[i] = -1;
   if (a.count && tid == 0) a.count[row] = n_sel;
