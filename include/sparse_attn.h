@@ -249,9 +249,9 @@ int sparse_attn_prefill_select(const void* q_idx, int q_dtype, const float* w,
  *     from sparse_attn_prefill_select, or from stages 1 and 2 run per
  *     sequence in chunks of query rows through a [chunk, L] score buffer in
  *     the workspace (the same sets) where that is faster on MI355X: T >= 2048
- *     with L >= 16384 (and k in the top-k set), and every L above the fused
- *     select's 32768.  A chunk holds as many query rows as 1 GiB of scores
- *     does, at least 4096 (at most T).
+ *     with L >= 2048, or T >= 1024 with L > 16384 (k in the top-k set), and
+ *     every L above the fused select's 32768.  A chunk holds as many query
+ *     rows as 1 GiB of scores does, at least 4096 (at most T).
  *   mode SA_PREFILL_DENSE: stage 3 over every candidate position s <
  *     min(q_pos[b,t] + 1, kv_len[b], L), with no indexer and no Top-K: the
  *     dense attention with a causal mask that "LLM注意力优化：稀疏注意力" (DSA

@@ -289,8 +289,11 @@ def test_prefill_dense_fullsize_sampled():
     # many query rows as 1 GiB of scores holds (4096 at L = 65536), so each
     # sequence runs 4096 + 104 rows
     (2, 4200, 65536),
-    # T >= 2048 with L >= 16384: staged (faster there), one chunk of T rows
+    # staged where measured faster, one chunk of T rows: T >= 2048 with
+    # L >= 2048, and T >= 1024 with L > 16384
     (1, 2100, 20000),
+    (2, 2300, 3000),
+    (1, 1100, 20000),
 ])
 def test_prefill_sparse_staged_select(B, T, L):
     _announce(f"prefill sparse B={B} T={T} L={L} (staged select)")

@@ -142,14 +142,16 @@ int index_and_select(sa::IndexerArgs ia, const sa::TopkArgs& ta, void* topk_ws, 
 // The prefill select runs staged (stage 1 into a score buffer, then stage 2)
 // where that is faster than the fused select, and wherever rows are longer
 // than the fused select holds on chip.  Measured on MI355X (k = 2048, H^I =
-// 64, d^I = 128, bf16, the last T queries of an L-token context): staged
-// 1.08 ms against 1.17 fused at T = 4096, L = 16384, and 1.10 against 2.18
-// at T = 2048, L = 32768 (the fused select keeps one row per work-group
-// there); the fused select is faster with fewer query rows (0.35 against
-// 0.51 ms at T = 1024, L = 16384) or shorter rows (0.29 against 0.37 at
-// T = L = 4096).
+// 64, d^I = 128, bf16, the last T queries of an L-token context; fused vs
+// staged): 93 vs 99 us at T = L = 2048, 250 vs 300 at T = L = 4096, 1.03 vs
+// 1.19 ms at T = 4096, L = 16384, 2.48 vs 2.89 ms at T = L = 16384, 0.96 vs
+// 1.12 ms at T = 1024, L = 32768 (the fused select keeps one row per
+// work-group there); the fused select wins with fewer rows: 111 vs 153 us at
+// T = 1024, L = 4096, 346 vs 496 us at T = 1024, L = 16384, and by nearly 3x
+// at T <= 256.
 constexpr int kPrefillStagedMinRows = 2048;
-constexpr int kPrefillStagedMinL = 16384;
+constexpr int kPrefillStagedMinL = 2048;
+constexpr int kPrefillStagedLongRows = 1024;  // rows per sequence when L > 16384
 // Staged chunks of query rows per sequence: as many as a 1 GiB score buffer
 // holds, at least 4096 (512 score work-groups, enough to fill the GPU), at
 // most T.  One chunk keeps the score kernel's heaviest-rows-first order over
@@ -157,9 +159,11 @@ constexpr int kPrefillStagedMinL = 16384;
 constexpr size_t kPrefillScoreBudget = 1ull << 30;
 constexpr int kPrefillChunkRows = 4096;
 bool prefill_staged(int T, int L, int k) {
-  return T > 0 && (L > sa::kPrefillSelectMaxL ||
-                   (T >= kPrefillStagedMinRows && L >= kPrefillStagedMinL &&
-                    sa::topk_supported(L, k)));
+  if (T <= 0) return false;
+  if (L > sa::kPrefillSelectMaxL) return true;
+  return sa::topk_supported(L, k) &&
+         ((T >= kPrefillStagedMinRows && L >= kPrefillStagedMinL) ||
+          (T >= kPrefillStagedLongRows && L > 16384));
 }
 
 // prefill workspace layout: idx [B, T, k] | count [B, T] | mla ws (the larger

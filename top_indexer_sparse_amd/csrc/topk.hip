@@ -8,9 +8,11 @@
 //
 // Method (one 1024-thread work-group per row):
 //  1. Each score becomes an order-preserving 32-bit key (-0 folded onto +0;
-//     NaN and -inf become key 0, "not a candidate").  Wave w holds positions
-//     [2048 w, 2048 w + 2048) in registers, loaded as 16-byte vectors: lane l,
-//     round i, element e is position 2048 w + 4 (l + 64 i) + e.
+//     NaN and -inf become key 0, "not a candidate").  The keys sit in LDS by
+//     position; wave w owns positions [256 nr w, 256 nr (w + 1)), nr rounds
+//     of 256 (nr = the fewest rounds that cover the row, at most 8), read as
+//     16-byte vectors: lane l, round i, element e is position
+//     256 nr w + 4 (l + 64 i) + e.
 //  2. tau = the k-th largest key.  Keys are binned by a digit fitted to the
 //     row, d = (key - min key) >> sh, with sh chosen so that the key range
 //     spans at most 2048 bins (index scores share sign and exponent, so fixed
@@ -49,7 +51,6 @@ constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkSeg = 32;                   // keys per thread
 constexpr int kTkRounds = kTkSeg / 4;        // 16-byte loads per thread
 constexpr int kTkRow = kTkThreads * kTkSeg;  // 32768 positions per work-group
-constexpr int kTkWaveSpan = kTkRow / kTkWaves;
 constexpr int kTkBins = 2048;
 constexpr int kTkAux = 5120;  // bracket candidates held in LDS (>= kTopkMaxK)
 
@@ -188,19 +189,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
     out_count = a.count ? a.count + bt : nullptr;
   }
 
-  // ---- scores into LDS by DMA; wave w fills positions [2048 w, 2048 w + 2048)
-  const int wbase4 = wave * (kTkWaveSpan / 4);  // in 16-byte units
+  // ---- scores into LDS by DMA; wave w fills positions [256 nr w, 256 nr (w + 1)),
+  // nr rounds of 256 positions (as few as cover the row: a short row keeps
+  // every wave busy instead of leaving most of them looping over empty slots)
+  const int nr = min(kTkRounds, max(1, (n + 256 * kTkWaves - 1) / (256 * kTkWaves)));
+  const int wbase4 = wave * 64 * nr;  // in 16-byte units
   const uint32_t lds_keys = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)&keys4[0];
   const uint8_t* gsrc = reinterpret_cast<const uint8_t*>(src);
   if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-    for (int i = 0; i < kTkRounds; ++i) {  // 16 bytes per lane, 1 KB per wave
+    for (int i = 0; i < nr; ++i) {  // 16 bytes per lane, 1 KB per wave
       const int u = wbase4 + 64 * i;
       if (4 * (u + lane) + 3 < n) dma16(gsrc, 16u * (uint32_t)(u + lane), lds_keys + 16u * (uint32_t)u);
     }
     const int n4 = n & ~3;  // the ragged end: up to 3 scores, one dword each
     if (wave == 0 && lane < n - n4) dma4(gsrc, 4u * (uint32_t)(n4 + lane), lds_keys + 4u * (uint32_t)n4);
   } else {
-    for (int i = 0; i < 4 * kTkRounds; ++i) {  // 4 bytes per lane
+    for (int i = 0; i < 4 * nr; ++i) {  // 4 bytes per lane
       const int p = 4 * wbase4 + 64 * i;
       if (p + lane < n) dma4(gsrc, 4u * (uint32_t)(p + lane), lds_keys + 4u * (uint32_t)p);
     }
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
     uint32_t mn = 0xffffffffu, mx = 0u;
     int nv = 0;
 #pragma unroll 2
-    for (int i = 0; i < kTkRounds; ++i) {
+    for (int i = 0; i < nr; ++i) {
       const int u = wbase4 + lane + 64 * i;
       uint4 q = keys4[u];
       uint32_t kk[4] = {q.x, q.y, q.z, q.w};
@@ -265,12 +269,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
       int s2 = 0;
       uint32_t dmask = 0u;
       if (mode == kSample) {
-        // one key per lane, spread over the wave's eight rounds
-        const uint32_t key = keys[4 * (wbase4 + lane + 64 * (lane & 7)) + ((lane >> 3) & 3)];
+        // one key per lane, spread over the wave's rounds
+        const uint32_t key = keys[4 * (wbase4 + lane + 64 * ((lane & 7) % nr)) + ((lane >> 3) & 3)];
         hist_add(hist, (key - kmin) >> sh, key != 0u);
       } else if (mode == kAll) {
         #pragma unroll 1
-        for (int i = 0; i < kTkRounds; ++i) {
+        for (int i = 0; i < nr; ++i) {
           const uint4 q = keys4[wbase4 + lane + 64 * i];
           const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
           }
         } else {  // kFilter: the bracket outgrew aux; filter the whole row
           #pragma unroll 1
-          for (int i = 0; i < kTkRounds; ++i) {
+          for (int i = 0; i < nr; ++i) {
             const uint4 q = keys4[wbase4 + lane + 64 * i];
             const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
         if (mode == kSample) {
           int ab = 0, in = 0;
           #pragma unroll 1
-          for (int i = 0; i < kTkRounds; ++i) {
+          for (int i = 0; i < nr; ++i) {
             const uint4 q = keys4[wbase4 + lane + 64 * i];
             const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
         if (in_me < 0) {
           in_me = 0;
           #pragma unroll 1
-          for (int i = 0; i < kTkRounds; ++i) {
+          for (int i = 0; i < nr; ++i) {
             const uint4 q = keys4[wbase4 + lane + 64 * i];
             in_me += (q.x != 0u && q.x >= lo_key && q.x <= hi_key) +
                      (q.y != 0u && q.y >= lo_key && q.y <= hi_key) +
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
         }
         int slot = block_scan_incl(in_me, red, ncand) - in_me;
         #pragma unroll 1
-        for (int i = 0; i < kTkRounds && in_me > 0; ++i) {
+        for (int i = 0; i < nr && in_me > 0; ++i) {
           const uint4 q = keys4[wbase4 + lane + 64 * i];
           const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
   // 256 per wave); a DPP scan gives the lanes below and the wave's total.
   int wtot = 0;
   #pragma unroll 1
-  for (int i = 0; i < kTkRounds; ++i) {
+  for (int i = 0; i < nr; ++i) {
     const uint4 q = keys4[wbase4 + lane + 64 * i];
     const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
     int c = 0;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
   int run = 0;  // packed counts of the waves before this one
   for (int w = 0; w < wave; ++w) run += red[w];
   #pragma unroll 1
-  for (int i = 0; i < kTkRounds; ++i) {
+  for (int i = 0; i < nr; ++i) {
     const int u = wbase4 + lane + 64 * i;
     const uint4 q = keys4[u];
     const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
