@@ -322,8 +322,9 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w,
  *
  * sparse_attn_block_pool: krep[b, n, g, :] = mean over the blk tokens of block
  * n of k[b, :, g, :], for the complete blocks n < L / blk.
- *   k [B, L, Hkv, d] bf16; krep [B, L/blk, Hkv, d] fp32 output (may be NULL
- *   when L < blk: there is no complete block).
+ *   k [B, L, Hkv, d] bf16; krep [B, L/blk, Hkv, d] bf16 output, the fp32 mean
+ *   rounded to nearest even (may be NULL when L < blk: there is no complete
+ *   block).
  *
  * sparse_attn_block_decode: per query head h (KV head g = h / (Hq / Hkv)):
  *   block score n = q[b,h,:] . krep[b,n,g,:]; the nsel highest (ties to the
@@ -347,10 +348,10 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w,
  * empty (L < blk, no sinks, no window) gets out = 0.
  * ------------------------------------------------------------------------- */
 int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d,
-                           int blk, float* krep, void* stream);
+                           int blk, void* krep, void* stream);
 
 int sparse_attn_block_decode(const void* q, const void* k, const void* v,
-                             const float* krep, int B, int L, int Hq, int Hkv,
+                             const void* krep, int B, int L, int Hq, int Hkv,
                              int d, int blk, int nsel, int n_sink, int n_win,
                              float sm_scale, int shared_choice, float* out,
                              int32_t* blocks_out, void* ws, size_t ws_bytes,

@@ -398,12 +398,13 @@ def sparse_attn_csa_decode(q_idx, w, k_idx, k_scale, n_comp, topk, q, comp, win,
 
 
 def sparse_attn_block_pool(k, blk, krep=None, stream=None):
-    """Mean-pooled block keys krep [B, L//blk, Hkv, d] fp32."""
+    """Mean-pooled block keys krep [B, L//blk, Hkv, d] bf16 (the fp32 mean,
+    rounded to nearest even)."""
     B, L, Hkv, d = k.shape
     _need(k, "k", (torch.bfloat16,))
     if krep is None:
-        krep = torch.empty((B, L // blk, Hkv, d), dtype=torch.float32, device=k.device)
-    _need(krep, "krep", (torch.float32,), (B, L // blk, Hkv, d))
+        krep = torch.empty((B, L // blk, Hkv, d), dtype=torch.bfloat16, device=k.device)
+    _need(krep, "krep", (torch.bfloat16,), (B, L // blk, Hkv, d))
     _call("sparse_attn_block_pool", _ptr(k), B, L, Hkv, d, blk, _ptr(krep) if krep.numel() else None,
           _stream(stream))
     return krep
@@ -418,7 +419,7 @@ def sparse_attn_block_decode(q, k, v, krep, blk, nsel, n_sink, n_win, sm_scale, 
     _need(q, "q", (torch.bfloat16,))
     _need(k, "k", (torch.bfloat16,), (B, L, Hkv, d))
     _need(v, "v", (torch.bfloat16,), (B, L, Hkv, d))
-    _need(krep, "krep", (torch.float32,), (B, L // blk, Hkv, d))
+    _need(krep, "krep", (torch.bfloat16,), (B, L // blk, Hkv, d))
     dev = q.device
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)

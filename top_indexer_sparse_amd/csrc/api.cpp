@@ -466,7 +466,7 @@ int sparse_attn_csa_decode(const void* q_idx, int q_idx_dtype, const float* w, c
   return s;
 }
 
-int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, float* krep,
+int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, void* krep,
                            void* stream) {
   clear_error();
   REQUIRE(B >= 0 && L >= 0 && Hkv >= 1 && blk >= 1, SA_ERR_SHAPE, "block_pool: bad size");
@@ -478,7 +478,7 @@ int sparse_attn_block_pool(const void* k, int B, int L, int Hkv, int d, int blk,
   return hip_status(sa::launch_block_pool(k, B, L, Hkv, d, blk, krep, (hipStream_t)stream), "block_pool launch");
 }
 
-int sparse_attn_block_decode(const void* q, const void* k, const void* v, const float* krep, int B,
+int sparse_attn_block_decode(const void* q, const void* k, const void* v, const void* krep, int B,
                              int L, int Hq, int Hkv, int d, int blk, int nsel, int n_sink,
                              int n_win, float sm_scale, int shared_choice, float* out,
                              int32_t* blocks_out, void* ws, size_t ws_bytes, void* stream) {

@@ -13,11 +13,12 @@
 //
 // Three kernels:
 //  * block_pool_kernel: one work-group per (block, sequence); 8-byte bf16
-//    loads, fp32 sums.  A cache-maintenance step (the pooled keys of a block
+//    loads, fp32 sums, the mean stored as bf16 (round to nearest even), the
+//    keys' own type.  A cache-maintenance step (the pooled keys of a block
 //    change only when the block fills), not part of a decode step.
 //  * block_score_kernel: one work-group per (64 blocks, KV head, sequence).
-//    Each pooled-key row (512 bytes) is read once, coalesced, by half a wave
-//    (16 bytes per lane) and scored against every query head of the KV group
+//    Each pooled-key row (256 bytes) is read once, coalesced, by half a wave
+//    (8 bytes per lane, widened to fp32) and scored against every query head of the KV group
 //    (or, with a shared choice, their sum); the per-lane partial dot products
 //    are summed over the half wave.  Scores go to the workspace, [B, Hq, nblk].
 //  * block_attn_kernel: one work-group per (query head, sequence).  It first
@@ -60,11 +61,11 @@ size_t block_workspace_bytes(int B, int Hq, int L, int nsel, int Hkv, int d, int
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restrict__ k, int L,
                                                          int E, int blk,
-                                                         float* __restrict__ krep) {
+                                                         uint16_t* __restrict__ krep) {
   const int n = blockIdx.x, b = blockIdx.y;
   const int nblk = L / blk;
   const uint16_t* src = k + ((int64_t)b * L + (int64_t)n * blk) * E;
-  float* dst = krep + ((int64_t)b * nblk + n) * E;
+  uint16_t* dst = krep + ((int64_t)b * nblk + n) * E;
   const float inv = 1.f / (float)blk;
   for (int e = 4 * threadIdx.x; e < E; e += 4 * 256) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -76,7 +77,8 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const uint16_t* __restr
       a2 += bf16_lo(u.y);
       a3 += bf16_hi(u.y);
     }
-    *(float4*)(dst + e) = make_float4(a0 * inv, a1 * inv, a2 * inv, a3 * inv);
+    // the fp32 mean, rounded to nearest even bf16
+    *(uint2*)(dst + e) = make_uint2(pack_bf16x2_rne(a0 * inv, a1 * inv), pack_bf16x2_rne(a2 * inv, a3 * inv));
   }
 }
 
@@ -92,7 +94,7 @@ __device__ __forceinline__ uint32_t blk_score_key(float f) {
 
 struct BlockScoreArgs {
   const uint16_t* q;    // [B, Hq, d]
-  const float* krep;    // [B, nblk, Hkv, d]
+  const uint16_t* krep;  // [B, nblk, Hkv, d] bf16
   int Hq, Hkv, nblk;
   int shared;           // score with the sum of the KV group's queries
   float* scores;        // [B, Hq, nblk] (workspace)
@@ -147,11 +149,11 @@ __global__ __launch_bounds__(256) void block_score_kernel(BlockScoreArgs a) {
       for (int c = 0; c < 4; ++c) qv[0][c] += qv[hh][c];
   }
   const int n0 = blockIdx.x * kScoreBlocks + 16 * wave + e;
-  float4 kv[8];
+  uint2 kv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int n = min(n0 + 2 * i, nblk - 1);
-    kv[i] = *(const float4*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD + 4 * l);
+    kv[i] = *(const uint2*)(a.krep + (((int64_t)b * nblk + n) * a.Hkv + g) * kBlkD + 4 * l);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -161,10 +163,10 @@ __global__ __launch_bounds__(256) void block_score_kernel(BlockScoreArgs a) {
     for (int hh = 0; hh < G; ++hh) {
       p[hh] = 0.f;
       if (a.shared && hh > 0) continue;  // uniform: one summed query
-      float acc = kv[i].x * qv[hh][0];
-      acc = fmaf(kv[i].y, qv[hh][1], acc);
-      acc = fmaf(kv[i].z, qv[hh][2], acc);
-      acc = fmaf(kv[i].w, qv[hh][3], acc);
+      float acc = bf16_lo(kv[i].x) * qv[hh][0];
+      acc = fmaf(bf16_hi(kv[i].x), qv[hh][1], acc);
+      acc = fmaf(bf16_lo(kv[i].y), qv[hh][2], acc);
+      acc = fmaf(bf16_hi(kv[i].y), qv[hh][3], acc);
       p[hh] = half_wave_sum(acc);
     }
     if (n < nblk && l < G) {  // lane l of the half wave writes head g G + l
@@ -509,11 +511,12 @@ __global__ __launch_bounds__(256) void block_attn_kernel(BlockAttnArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, float* krep,
+hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d, int blk, void* krep,
                              hipStream_t st) {
   const int nblk = L / blk;
   if (B == 0 || nblk == 0) return hipSuccess;
-  block_pool_kernel<<<dim3(nblk, B), 256, 0, st>>>((const uint16_t*)k, L, Hkv * d, blk, krep);
+  block_pool_kernel<<<dim3(nblk, B), 256, 0, st>>>((const uint16_t*)k, L, Hkv * d, blk,
+                                                   (uint16_t*)krep);
   return hipGetLastError();
 }
 
@@ -524,7 +527,7 @@ hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st) {
   if (nblk > 0) {
     BlockScoreArgs c{};
     c.q = (const uint16_t*)a.q;
-    c.krep = a.krep;
+    c.krep = (const uint16_t*)a.krep;
     c.Hq = a.Hq;
     c.Hkv = a.Hkv;
     c.nblk = nblk;

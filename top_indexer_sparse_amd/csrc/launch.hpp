@@ -117,7 +117,7 @@ struct BlockArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* krep;
+  const void* krep;  // bf16 pooled block keys
   int B, L, Hq, Hkv, d, blk, nsel, n_sink, n_win;
   float sm_scale;
   int shared_choice;  // 1: one block choice per KV group (sum of its heads' scores)
@@ -128,7 +128,7 @@ struct BlockArgs {
 bool block_supported(const BlockArgs& a);
 size_t block_workspace_bytes(int B, int Hq, int L, int nsel, int Hkv, int d, int blk);
 hipError_t launch_block_pool(const void* k, int B, int L, int Hkv, int d,
-                             int blk, float* krep, hipStream_t st);
+                             int blk, void* krep, hipStream_t st);
 hipError_t launch_block_decode(const BlockArgs& a, hipStream_t st);
 
 }  // namespace sa
