@@ -160,6 +160,8 @@ def _check_decode(q, w, k, k_scale, kv_len, topk, expect=None):
     ("clustered", 32, 32768, 2048, None, "reread"),  # the benchmark's launch geometry
     ("phase", 4, 32768, 2048, None, "reread"),
     ("phase", 32, 32768, 2048, None, "reread"),
+    # read back with ragged candidate limits (and rows with at most k candidates)
+    ("phase", 6, 32768, 2048, [32768, 20000, 9000, 2048, 1, 0], "reread"),
     # the keys above the read-back bound outgrow LDS: the score row is read
     ("halfphase", 32, 32768, 2048, None, "row"),
     ("ties", 3, 20037, 512, None, "lists"),
@@ -248,6 +250,17 @@ def test_decode_select_never_takes_nan_scores(nnan, path):
         assert np.array_equal(np.sort(fin[oi[0, 0][oi[0, 0] >= 0]]), sel)
     paths = [select_path(s.cpu().numpy()[b, 0], L, k, B, L) for b in range(B)]
     assert path in paths, paths
+
+
+def test_decode_select_fp8_keys_read_back():
+    # fp8 keys whose per-token scale is 4x on one 64-position phase of every
+    # 1024: the read-back path reads scaled scores, as the lists hold them
+    _announce("decode select fp8 keys, phase pattern through the scales, B=3 L=40000")
+    wl = workloads.decode_128k_fp8(B=3, L=40000)
+    scale = wl.k_scale.clone()
+    pos = torch.arange(wl.L)
+    scale[:, (pos % 1024) < 64] *= 4
+    _check_decode(wl.q_idx, wl.w, wl.k_idx, scale, wl.kv_len, wl.topk, expect="reread")
 
 
 def test_decode_select_fp8_keys():
