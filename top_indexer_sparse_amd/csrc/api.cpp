@@ -142,13 +142,14 @@ int index_and_select(sa::IndexerArgs ia, const sa::TopkArgs& ta, void* topk_ws, 
 // The prefill select runs staged (stage 1 into a score buffer, then stage 2)
 // where that is faster than the fused select, and wherever rows are longer
 // than the fused select holds on chip.  Measured on MI355X (k = 2048, H^I =
-// 64, d^I = 128, bf16, the last T queries of an L-token context; fused vs
-// staged): 93 vs 99 us at T = L = 2048, 250 vs 300 at T = L = 4096, 1.03 vs
-// 1.19 ms at T = 4096, L = 16384, 2.48 vs 2.89 ms at T = L = 16384, 0.96 vs
-// 1.12 ms at T = 1024, L = 32768 (the fused select keeps one row per
-// work-group there); the fused select wins with fewer rows: 111 vs 153 us at
-// T = 1024, L = 4096, 346 vs 496 us at T = 1024, L = 16384, and by nearly 3x
-// at T <= 256.
+// 64, d^I = 128, bf16, the last T queries of an L-token context), staged
+// against fused: 93 against 99 us at T = L = 2048, 250 against 300 at T = L
+// = 4096, 1.03 against 1.19 ms at T = 4096, L = 16384, 2.48 against 2.89 ms
+// at T = L = 16384, 0.96 against 1.12 ms at T = 1024, L = 32768 (the fused
+// select keeps one row per work-group there).  The fused select wins with
+// fewer rows: 111 against 153 us (fused against staged) at T = 1024, L =
+// 4096, 346 against 496 us at T = 1024, L = 16384, and by nearly 3x at
+// T <= 256.
 constexpr int kPrefillStagedMinRows = 2048;
 constexpr int kPrefillStagedMinL = 2048;
 constexpr int kPrefillStagedLongRows = 1024;  // rows per sequence when L > 16384
