@@ -60,11 +60,13 @@ def test_indexer_mfma_decode(HI, dI, fp8):
     assert_scores_close(g, ref, fl)
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_indexer_mfma_prefill(fp8):
-    _announce(f"indexer prefill L=520 fp8={fp8}")
+@pytest.mark.parametrize("fp8,dI", [(False, 128), (True, 128), (False, 64), (True, 64)])
+def test_indexer_mfma_prefill(fp8, dI):
+    # the staged score kernel's key tiles: 16, 8, 8 and 4 KB per 64 positions
+    # (every wave, or only the first four, issues a 1 KB copy per block)
+    _announce(f"indexer prefill L=520 fp8={fp8} dI={dI}")
     L = 520
-    wl = workloads.prefill_16k(L=L, with_mla=False, n_needles=0)
+    wl = workloads.prefill_16k(L=L, dI=dI, with_mla=False, n_needles=0)
     k_idx, k_scale = wl.k_idx, None
     if fp8:
         k32 = wl.k_idx.float()
