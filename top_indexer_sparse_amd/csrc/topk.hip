@@ -139,15 +139,26 @@ struct TopkRowArgs {
 // MERGE = false: virtual row = positions [chunk*kTkRow, ...) of a score row.
 // MERGE = true : virtual row = the nchunks*k candidates of a row.
 //
+// CAP: positions a work-group holds.  CAP = kTkRow takes 128 KB of LDS for the
+// keys, one work-group per CU.  CAP = kTkRow / 2 (rows of at most 16384) fits
+// two work-groups per CU (under 80 KB each, 64 VGPRs per lane), so one row's
+// barrier and load waits overlap the other's work; its bracket buffer is
+// smaller (a fuller bracket takes the filter passes) and the selected
+// positions are stored straight to memory instead of through it.
+//
 // Code size matters here: a work-group runs its row once, usually on a CU
 // whose instruction cache is cold, so every 64 bytes of straight-line code
 // cost a fetch from L2.  The keys therefore live in LDS, arrive there by
 // global->LDS DMA (no registers, no unrolling), and every phase is a short
 // loop; all histogram rounds share one rank search.
-template <bool MERGE>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
-  __shared__ uint4 keys4[kTkRow / 4];  // the row's keys by position
-  __shared__ uint32_t aux[kTkAux];     // bracket candidates, then output positions
+template <bool MERGE, int CAP>
+__global__ __launch_bounds__(kTkThreads, CAP == kTkRow ? 1 : 8) void topk_kernel(TopkRowArgs a) {
+  constexpr bool kHalf = CAP != kTkRow;
+  constexpr int AUX = kHalf ? 1792 : kTkAux;  // bracket candidates (and, full size, outputs)
+  constexpr int RMAX = CAP / (256 * kTkWaves);  // rounds of 256 positions per wave
+  static_assert(CAP == kTkRow || CAP == kTkRow / 2, "row capacity");
+  __shared__ uint4 keys4[CAP / 4];  // the row's keys by position
+  __shared__ uint32_t aux[AUX];     // bracket candidates, then output positions
   __shared__ int hist[kTkBins];
   __shared__ int red[kTkWaves];
   __shared__ uint32_t rmin[kTkWaves], rmax[kTkWaves];
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
     const int b = (int)(bt / a.T);
     const int lim = candidate_limit(a.q_pos, a.kv_len, b, bt, a.L);
     pos_base = chunk * kTkRow;
-    n = min(max(lim - pos_base, 0), kTkRow);
+    n = min(max(lim - pos_base, 0), CAP);
     src = a.scores + bt * a.L + pos_base;
     if (a.nchunks == 1) {
       out_idx = a.idx + bt * k;
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
   // ---- scores into LDS by DMA; wave w fills positions [256 nr w, 256 nr (w + 1)),
   // nr rounds of 256 positions (as few as cover the row: a short row keeps
   // every wave busy instead of leaving most of them looping over empty slots)
-  const int nr = min(kTkRounds, max(1, (n + 256 * kTkWaves - 1) / (256 * kTkWaves)));
+  const int nr = min(RMAX, max(1, (n + 256 * kTkWaves - 1) / (256 * kTkWaves)));
   const int wbase4 = wave * 64 * nr;  // in 16-byte units
   const uint32_t lds_keys = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4*)&keys4[0];
   const uint8_t* gsrc = reinterpret_cast<const uint8_t*>(src);
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
         hi_key = (uint32_t)min((uint64_t)0xffffffffu, (uint64_t)lo_key + crange);
         top = crange ? 63 - __clzll((long long)crange) : -1;
         if (top < 0) break;  // the bracket is a single key value
-        if (inside > kTkAux) {
+        if (inside > AUX) {
           mode = kFilter;
           continue;
         }
@@ -433,21 +444,36 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(TopkRowArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool g = kk[e] > tau, eq = (kk[e] == tau) & (kk[e] != 0u);
-        if (g || (eq && eqb < need_eq)) aux[gtb + min(eqb, need_eq)] = (uint32_t)(4 * u + e);
+        if (g || (eq && eqb < need_eq)) {
+          const int slot = gtb + min(eqb, need_eq), p = 4 * u + e;
+          if constexpr (kHalf) {  // straight to memory
+            out_idx[slot] = vpos ? vpos[p] : pos_base + p;
+            if (out_score) out_score[slot] = key_score(kk[e]);
+          } else {
+            aux[slot] = (uint32_t)p;
+          }
+        }
         gtb += g;
         eqb += eq;
       }
     }
   }
-  __syncthreads();
-  for (int i = tid; i < k; i += kTkThreads) {
-    if (i < n_sel) {
-      const int v = min((int)aux[i], n - 1);  // (a slot is always < n)
-      out_idx[i] = vpos ? vpos[v] : pos_base + v;
-      if (out_score) out_score[i] = key_score(keys[v]);
-    } else {
+  if constexpr (kHalf) {
+    for (int i = n_sel + tid; i < k; i += kTkThreads) {
       out_idx[i] = -1;
       if (out_score) out_score[i] = -INFINITY;
+    }
+  } else {
+    __syncthreads();
+    for (int i = tid; i < k; i += kTkThreads) {
+      if (i < n_sel) {
+        const int v = min((int)aux[i], n - 1);  // (a slot is always < n)
+        out_idx[i] = vpos ? vpos[v] : pos_base + v;
+        if (out_score) out_score[i] = key_score(keys[v]);
+      } else {
+        out_idx[i] = -1;
+        if (out_score) out_score[i] = -INFINITY;
+      }
     }
   }
   if (out_count && tid == 0) *out_count = n_sel;
@@ -1100,10 +1126,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     r.cand_score = (float*)a.ws;
     r.cand_pos = (int32_t*)((char*)a.ws + sizeof(float) * rows * r.nchunks * a.k);
   }
-  topk_kernel<false><<<dim3(r.nchunks, (unsigned)rows), kTkThreads, 0, st>>>(r);
+  if (r.nchunks == 1 && a.L <= kTkRow / 2)  // two work-groups per CU
+    topk_kernel<false, kTkRow / 2><<<dim3(1, (unsigned)rows), kTkThreads, 0, st>>>(r);
+  else
+    topk_kernel<false, kTkRow><<<dim3(r.nchunks, (unsigned)rows), kTkThreads, 0, st>>>(r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r.nchunks == 1) return e;
-  topk_kernel<true><<<dim3(1, (unsigned)rows), kTkThreads, 0, st>>>(r);
+  topk_kernel<true, kTkRow><<<dim3(1, (unsigned)rows), kTkThreads, 0, st>>>(r);
   return hipGetLastError();
 }
 
