@@ -112,19 +112,20 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // MFMA paths
 // ---------------------------------------------------------------------------
 // One query per grid row; the query's waves share its positions chunk by
-// chunk.  Each wave streams its chunks through a register ring of R key chunks
-// (16 positions each), so R - 1 chunks (28 KB of bf16 keys per wave at R = 8)
-// stay in flight while one is consumed; R shrinks to 4 where the query block
-// alone takes half the registers (H^I x d^I = 128 x 128).  The loop body is free of conditional memory operations: ring
-// loads are always issued (rows past the range are clamped to its last valid
-// row and their scores ignored), and scores go to a per-wave LDS buffer, so
-// the compiler's vmcnt waits count exactly the older chunk's loads instead of
-// draining the ring.  The scores (times the fp8 scale) leave with coalesced
-// stores after the loop.
-constexpr int kDecMaxRing = 8;
-constexpr int kDecBuf = kDecMaxSpan + 16 * kDecMaxRing;  // + the ring's overrun
-template <int HT, int DI>
-constexpr int dec_ring() { return 16 * HT * DI >= 16384 ? 4 : kDecMaxRing; }
+// chunk.  A chunk is 16 consecutive key rows, one contiguous run of 16 x
+// ROWB bytes, and each wave moves its chunks into a ring of R LDS slots of
+// its own with global->LDS copies of 1 KB each: every copy covers whole
+// 128-byte lines, where a load straight into B-operand registers covers 16
+// rows x 64 bytes (half a line per row), and the key path holds no
+// registers.  A slot stores row r's
+// 16-byte piece p at piece p ^ (r mod pieces-per-row), so the B-operand reads
+// of 16 rows at one piece hit distinct banks.  The loop body is free of
+// conditional memory operations: copies are always issued (rows past the
+// range are clamped to its last valid row and their scores ignored), and
+// scores go to a per-wave LDS buffer.  The scores (times the fp8 scale)
+// leave with coalesced stores after the loop.
+constexpr int kDecRing = 3;  // LDS slots per wave: two chunks in flight while one is read
+constexpr int kDecBuf = kDecMaxSpan + 16 * kDecRing;  // + the ring's overrun
 
 // With KEEP, the work-group also leaves its candidate list for the Top-K
 // select (IdxKeep): n_w candidates here (positions < lim with a key), of
@@ -143,11 +144,16 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   constexpr int HI = 16 * HT;
   constexpr int ROWB = FP8 ? DI : 2 * DI;  // bytes per key row
   constexpr int NSC = kDecMaxSpan / 64;    // prefetched scales per lane
-  constexpr int R = dec_ring<HT, DI>();
+  constexpr int R = kDecRing;
+  constexpr int CHB = 16 * ROWB;           // bytes per chunk
+  constexpr int NB = CHB / 1024;           // 1 KB copies per chunk
+  constexpr int PPR = ROWB / 16;           // 16-byte pieces per row
+  static_assert(NB == 1 || NB == 2 || NB == 4, "chunk of 1, 2 or 4 KB");
   __shared__ float sbuf[4][kDecBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t kring[4][R][CHB];
   const int64_t bt = blockIdx.y;
   const int b = (int)(bt / T);
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int lim = candidate_limit(q_pos, kv_len, b, bt, L);
   float* out = scores + bt * L;
@@ -164,7 +170,6 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   if (!KEEP && nch == 0) return;  // the candidate list needs every wave
   const uint8_t* kb = k + (int64_t)b * L * ROWB;
   auto pos_of = [&](int c, int j) { return 16 * (wq + c * W) + j; };
-  auto row_of = [&](int c) { return kb + (int64_t)min(pos_of(c, n), v_end - 1) * ROWB; };
 
   float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
   float* sb = sbuf[wave];
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
     // wait after the ring's first loads completes the older loads (query,
     // weights, scales) and leaves the ring in flight.  The loop is then
     // entered, as it is continued, with exactly the ring's loads outstanding,
-    // so each chunk's wait counts the R - 1 younger chunks.
+    // so each chunk's wait counts the copies of the R - 1 younger chunks.
     QueryRegs<HT, DI, FP8> qr;
     qr.load(q + bt * HI * DI, w + bt * HI, lane);
     if constexpr (FP8) {
@@ -182,20 +187,53 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
       for (int i = 0; i < NSC; ++i)
         scr[i] = scb[min(pos_of(4 * i + (lane >> 4), lane & 15), v_end - 1)];
     }
-    asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
-    KeyChunk<DI, FP8> ring[R];
+    // Copy e of a chunk fills the slot's 1 KB block e: lane l writes 16-byte
+    // position 64 e + l, row r = (64 e + l) / PPR, which holds piece
+    // (position mod PPR) ^ (r mod PPR) of key row min(chunk start + r,
+    // v_end - 1).  Rows and pieces are the same for every chunk.
+    int crow[NB], cpiece[NB];
 #pragma unroll
-    for (int i = 0; i < R; ++i) ring[i].load(row_of(i), g);
-    wait_vmcnt<R * KeyChunk<DI, FP8>::NL>();
+    for (int e = 0; e < NB; ++e) {
+      const int c = 64 * e + lane, r = c / PPR;
+      crow[e] = r;
+      cpiece[e] = 16 * ((c % PPR) ^ (r % PPR));
+    }
+    const uint32_t lring =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&kring[wave][0][0];
+    auto issue = [&](int c, int slot) {
+      const int p0 = 16 * (wq + c * W);
+      const uint8_t* src[NB];
+#pragma unroll
+      for (int e = 0; e < NB; ++e)
+        src[e] = kb + (int64_t)min(p0 + crow[e], v_end - 1) * ROWB + cpiece[e];
+      const uint32_t dst = lring + (uint32_t)(slot * CHB);
+      if constexpr (NB == 4) {
+        dma16x4_addr(src[0], src[1], src[2], src[3], dst);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NB; ++e) dma16_addr(src[e], dst + 1024u * e);
+      }
+    };
+    asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
+#pragma unroll
+    for (int i = 0; i < R; ++i) issue(i, i);
+    // the query, weights and scales (older than the ring) have landed
+    wait_vmcnt<R * NB>();
     for (int c0 = 0; c0 < nch; c0 += R) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int c = c0 + i;  // chunks past nch are computed and dropped
-        const float sc = qr.score(ring[i]);
+        wait_vmcnt<(R - 1) * NB>();  // chunk c landed; the younger ones may not have
+        asm volatile("" ::: "memory");
+        KeyChunk<DI, FP8> kc;
+        kc.load_swz(&kring[wave][i][n * ROWB], g, n & (PPR - 1));
+        const float sc = qr.score(kc);
         sb[16 * c + n] = sc;  // the four lane groups write the same value
-        ring[i].load(row_of(c + R), g);
+        wait_lgkm0();         // the slot's reads are done before it is refilled
+        issue(c + R, i);
       }
     }
+    wait_vmcnt<0>();  // no copy outlives the wave
   }
   // the wave's own LDS writes are ordered before these reads; slot i of a
   // lane is position j = lane % 16 of chunk 4 i + lane / 16 (64-byte runs)
