@@ -167,58 +167,89 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   const int W = gridDim.x * 4, wq = blockIdx.x * 4 + wave;
   const int nch_all = (v_end + 15) / 16;
   const int nch = wq < nch_all ? (nch_all - wq + W - 1) / W : 0;
-  if (!KEEP && nch == 0) return;  // the candidate list needs every wave
+  // no wave of the work-group has a chunk (the same for all four waves)
+  if (!KEEP && (int)blockIdx.x * 4 >= nch_all) return;
   const uint8_t* kb = k + (int64_t)b * L * ROWB;
   auto pos_of = [&](int c, int j) { return 16 * (wq + c * W) + j; };
 
-  float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
-  float* sb = sbuf[wave];
-  if (KEEP ? nch > 0 : true) {
-    // The query, the weights and the first R chunks go out together; the
-    // wait after the ring's first loads completes the older loads (query,
-    // weights, scales) and leaves the ring in flight.  The loop is then
-    // entered, as it is continued, with exactly the ring's loads outstanding,
-    // so each chunk's wait counts the copies of the R - 1 younger chunks.
-    QueryRegs<HT, DI, FP8> qr;
+  // Copy e of a chunk fills the slot's 1 KB block e: lane l writes 16-byte
+  // position 64 e + l, row r = (64 e + l) / PPR, which holds piece
+  // (position mod PPR) ^ (r mod PPR) of key row min(chunk start + r,
+  // v_end - 1).  Rows and pieces are the same for every chunk.
+  int crow[NB], cpiece[NB];
+#pragma unroll
+  for (int e = 0; e < NB; ++e) {
+    const int c = 64 * e + lane, r = c / PPR;
+    crow[e] = r;
+    cpiece[e] = 16 * ((c % PPR) ^ (r % PPR));
+  }
+  const uint32_t lring =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&kring[wave][0][0];
+  auto issue = [&](int c, int slot) {
+    const int p0 = 16 * (wq + c * W);
+    const uint8_t* src[NB];
+#pragma unroll
+    for (int e = 0; e < NB; ++e)
+      src[e] = kb + (int64_t)min(p0 + crow[e], v_end - 1) * ROWB + cpiece[e];
+    const uint32_t dst = lring + (uint32_t)(slot * CHB);
+    if constexpr (NB == 4) {
+      dma16x4_addr(src[0], src[1], src[2], src[3], dst);
+    } else {
+#pragma unroll
+      for (int e = 0; e < NB; ++e) dma16_addr(src[e], dst + 1024u * e);
+    }
+  };
+
+  // The query block goes out first, then the fp8 scales, then the ring's
+  // first R chunks; the wait after them completes the older loads and leaves
+  // the ring in flight.  The loop is then entered, as it is continued, with
+  // exactly the ring's copies outstanding, so each chunk's wait counts the
+  // copies of the R - 1 younger chunks.  A query block that fits the score
+  // buffer is copied there once per work-group (the four waves share it;
+  // row h's 16-byte piece p at p ^ (h mod d^I/8)) and read into registers
+  // before any score is written; a larger one is loaded by each wave.
+  constexpr int QB = 2 * HI * DI;  // query block bytes
+  constexpr int PPQ = DI / 8;      // 16-byte pieces per query row
+  constexpr bool QST = QB % 1024 == 0 && QB <= (int)sizeof(sbuf);
+  QueryRegs<HT, DI, FP8> qr;
+  if constexpr (QST) {
+    const uint8_t* qg = uniform_ptr((const uint8_t*)(q + bt * HI * DI));
+    const uint32_t lq =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&sbuf[0][0];
+    for (int e = wave; e < QB / 1024; e += 4) {
+      const int c = 64 * e + lane, r = c / PPQ;
+      dma16(qg, (uint32_t)(r * 2 * DI + 16 * ((c % PPQ) ^ (r % PPQ))), lq + 1024u * e);
+    }
+  } else {
     qr.load(q + bt * HI * DI, w + bt * HI, lane);
-    if constexpr (FP8) {
+  }
+  float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
+  if constexpr (FP8) {
+    if (nch > 0) {
       const float* scb = kscale + (int64_t)b * L;
 #pragma unroll
       for (int i = 0; i < NSC; ++i)
         scr[i] = scb[min(pos_of(4 * i + (lane >> 4), lane & 15), v_end - 1)];
     }
-    // Copy e of a chunk fills the slot's 1 KB block e: lane l writes 16-byte
-    // position 64 e + l, row r = (64 e + l) / PPR, which holds piece
-    // (position mod PPR) ^ (r mod PPR) of key row min(chunk start + r,
-    // v_end - 1).  Rows and pieces are the same for every chunk.
-    int crow[NB], cpiece[NB];
-#pragma unroll
-    for (int e = 0; e < NB; ++e) {
-      const int c = 64 * e + lane, r = c / PPR;
-      crow[e] = r;
-      cpiece[e] = 16 * ((c % PPR) ^ (r % PPR));
-    }
-    const uint32_t lring =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&kring[wave][0][0];
-    auto issue = [&](int c, int slot) {
-      const int p0 = 16 * (wq + c * W);
-      const uint8_t* src[NB];
-#pragma unroll
-      for (int e = 0; e < NB; ++e)
-        src[e] = kb + (int64_t)min(p0 + crow[e], v_end - 1) * ROWB + cpiece[e];
-      const uint32_t dst = lring + (uint32_t)(slot * CHB);
-      if constexpr (NB == 4) {
-        dma16x4_addr(src[0], src[1], src[2], src[3], dst);
-      } else {
-#pragma unroll
-        for (int e = 0; e < NB; ++e) dma16_addr(src[e], dst + 1024u * e);
-      }
-    };
-    asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
+  }
+  asm volatile("" ::: "memory");  // issued before the ring, as the waits assume
+  if (nch > 0) {
 #pragma unroll
     for (int i = 0; i < R; ++i) issue(i, i);
-    // the query, weights and scales (older than the ring) have landed
-    wait_vmcnt<R * NB>();
+    wait_vmcnt<R * NB>();  // the query and the scales (older than the ring) have landed
+  } else {
+    wait_vmcnt<0>();
+  }
+  if constexpr (QST) {
+    lds_barrier();  // every wave's query copies landed
+    qr.load_lds((const uint8_t*)&sbuf[0][0], w + bt * HI, lane);
+    wait_lgkm0();
+    lds_barrier();  // every wave holds its query registers: the score buffer is free
+  }
+  if (!KEEP && nch == 0) return;  // the candidate list needs every wave
+
+  float* sb = sbuf[wave];
+  if (nch > 0) {
     for (int c0 = 0; c0 < nch; c0 += R) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
