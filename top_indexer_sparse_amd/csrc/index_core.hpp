@@ -92,8 +92,8 @@ struct QueryRegs {
   }
   // The same operands from the query rows staged in LDS (qs), row h's
   // 16-byte piece p stored at piece p ^ (h mod d^I/8), and the weights from
-  // memory.
-  __device__ __forceinline__ void load_lds(const uint8_t* qs, const float* wrow, int lane) {
+  // LDS too (ws, one float per head).
+  __device__ __forceinline__ void load_lds(const uint8_t* qs, const float* ws, int lane) {
     constexpr int PPQ = DI / 8;  // 16-byte pieces per query row
     const int n = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -105,7 +105,7 @@ struct QueryRegs {
         a[ht][ks] = as_bf16x8(*(const uintx4*)(qs + h * 2 * DI + 16 * (p ^ (h % PPQ))));
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wr[ht][r] = wrow[16 * ht + 4 * g + r];
+      for (int r = 0; r < 4; ++r) wr[ht][r] = ws[16 * ht + 4 * g + r];
     }
   }
   // Score of position (s0 + l%16), summed over all heads, valid in every lane.

@@ -204,24 +204,37 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   // first R chunks; the wait after them completes the older loads and leaves
   // the ring in flight.  The loop is then entered, as it is continued, with
   // exactly the ring's copies outstanding, so each chunk's wait counts the
-  // copies of the R - 1 younger chunks.  A query block that fits the score
-  // buffer is copied there once per work-group (the four waves share it;
-  // row h's 16-byte piece p at p ^ (h mod d^I/8)) and read into registers
-  // before any score is written; a larger one is loaded by each wave.
+  // copies of the R - 1 younger chunks.  No load the compiler tracks may be
+  // pending when the loop is entered with a use inside it: the compiler
+  // cannot see the copies, so its own wait for such a load would count them
+  // as done and drain the ring on every pass.  A query block that fits the
+  // score buffer (with its weights) is therefore copied there once per
+  // work-group (the four waves share it; row h's 16-byte piece p at
+  // p ^ (h mod d^I/8), the weights after the block) and read into registers
+  // before any score is written; a larger one is loaded by each wave and
+  // waited for before the ring goes out.
   constexpr int QB = 2 * HI * DI;  // query block bytes
   constexpr int PPQ = DI / 8;      // 16-byte pieces per query row
-  constexpr bool QST = QB % 1024 == 0 && QB <= (int)sizeof(sbuf);
+  constexpr int NWC = (HI + 63) / 64;  // 256-byte weight copies
+  constexpr bool QST = QB % 1024 == 0 && QB + 256 * NWC <= (int)sizeof(sbuf);
   QueryRegs<HT, DI, FP8> qr;
   if constexpr (QST) {
     const uint8_t* qg = uniform_ptr((const uint8_t*)(q + bt * HI * DI));
+    const uint8_t* wg = uniform_ptr((const uint8_t*)(w + bt * HI));
     const uint32_t lq =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&sbuf[0][0];
     for (int e = wave; e < QB / 1024; e += 4) {
       const int c = 64 * e + lane, r = c / PPQ;
       dma16(qg, (uint32_t)(r * 2 * DI + 16 * ((c % PPQ) ^ (r % PPQ))), lq + 1024u * e);
     }
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < NWC; ++e)  // lanes past H^I repeat the last weight
+        dma4(wg, 4u * (uint32_t)min(64 * e + lane, HI - 1), lq + (uint32_t)QB + 256u * e);
+    }
   } else {
     qr.load(q + bt * HI * DI, w + bt * HI, lane);
+    wait_vmcnt<0>();
   }
   float scr[FP8 ? NSC : 1];  // fp8 per-token scales of this lane's output slots
   if constexpr (FP8) {
@@ -242,7 +255,8 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
   }
   if constexpr (QST) {
     lds_barrier();  // every wave's query copies landed
-    qr.load_lds((const uint8_t*)&sbuf[0][0], w + bt * HI, lane);
+    qr.load_lds((const uint8_t*)&sbuf[0][0], (const float*)((const uint8_t*)&sbuf[0][0] + QB),
+                lane);
     wait_lgkm0();
     lds_barrier();  // every wave holds its query registers: the score buffer is free
   }
