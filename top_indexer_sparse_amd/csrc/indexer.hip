@@ -124,7 +124,9 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // range are clamped to its last valid row and their scores ignored), and
 // scores go to a per-wave LDS buffer.  The scores (times the fp8 scale)
 // leave with coalesced stores after the loop.
-constexpr int kDecRing = 3;  // LDS slots per wave: two chunks in flight while one is read
+// LDS slots per wave.  A slot is refilled as soon as its chunk is in registers, so two
+// chunks are in flight during each chunk's contraction.
+constexpr int kDecRing = 2;
 constexpr int kDecBuf = kDecMaxSpan + 16 * kDecRing;  // + the ring's overrun
 
 // With KEEP, the work-group also leaves its candidate list for the Top-K
@@ -268,14 +270,14 @@ __global__ __launch_bounds__(256) void idx_decode_kernel(
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int c = c0 + i;  // chunks past nch are computed and dropped
-        wait_vmcnt<(R - 1) * NB>();  // chunk c landed; the younger ones may not have
+        wait_vmcnt<(R - 1) * NB>();  // chunk c landed; the younger one may not have
         asm volatile("" ::: "memory");
         KeyChunk<DI, FP8> kc;
         kc.load_swz(&kring[wave][i][n * ROWB], g, n & (PPR - 1));
+        wait_lgkm0();  // the slot's reads are done before it is refilled
+        issue(c + R, i);
         const float sc = qr.score(kc);
         sb[16 * c + n] = sc;  // the four lane groups write the same value
-        wait_lgkm0();         // the slot's reads are done before it is refilled
-        issue(c + R, i);
       }
     }
     wait_vmcnt<0>();  // no copy outlives the wave
