@@ -60,6 +60,37 @@ def test_indexer_mfma_decode(HI, dI, fp8):
     assert_scores_close(g, ref, fl)
 
 
+@pytest.mark.parametrize("HI,dI,fp8", [(64, 128, False), (128, 128, False), (64, 128, True),
+                                       (16, 64, True), (32, 64, False)])
+def test_decode_and_prefill_score_kernels_carry_the_same_bits(HI, dI, fp8):
+    # The decode score kernel (one query per row; keys and, where it fits, the
+    # query block staged through LDS) and the staged prefill score kernel (eight
+    # queries sharing LDS key tiles) compute the same contraction in the same
+    # order, so every score must match bit for bit.  L = 700 leaves ragged
+    # tails of both kernels' chunks and tiles.
+    _announce(f"indexer decode vs prefill bits HI={HI} dI={dI} fp8={fp8}")
+    B, T, L = 2, 8, 700
+    gen = torch.Generator().manual_seed(1000 * HI + dI + int(fp8))
+    q = torch.randn((B, T, HI, dI), generator=gen).to(torch.bfloat16)
+    w = torch.rand((B, T, HI), generator=gen)
+    k = torch.randn((B, L, dI), generator=gen)
+    ks = None
+    if fp8:
+        k = k.to(torch.float8_e4m3fn)
+        ks = 0.5 + torch.rand((B, L), generator=gen)
+    else:
+        k = k.to(torch.bfloat16)
+    q, w, k, ks = _cuda(q, w, k, ks)
+    qp = torch.full((B, T), L - 1, dtype=torch.int32, device=DEV)  # every position a candidate
+    pre = api.sparse_attn_indexer_scores(q, w, k, k_scale=ks, q_pos=qp)
+    dec = torch.cat([api.sparse_attn_indexer_scores(q[:, t:t + 1].contiguous(),
+                                                    w[:, t:t + 1].contiguous(), k, k_scale=ks)
+                     for t in range(T)], dim=1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(pre).all()
+    assert torch.equal(pre.view(torch.int32), dec.view(torch.int32)), "score bits differ"
+
+
 @pytest.mark.parametrize("fp8,dI", [(False, 128), (True, 128), (False, 64), (True, 64)])
 def test_indexer_mfma_prefill(fp8, dI):
     # the staged score kernel's key tiles: 16, 8, 8 and 4 KB per 64 positions
