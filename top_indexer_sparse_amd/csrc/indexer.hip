@@ -112,20 +112,19 @@ __global__ __launch_bounds__(256) void idx_vector_kernel(
 // MFMA paths
 // ---------------------------------------------------------------------------
 // One query per grid row; the query's waves share its positions chunk by
-// chunk.  A chunk is 16 consecutive key rows, one contiguous run of 16 x
-// ROWB bytes, and each wave moves its chunks into a ring of R LDS slots of
-// its own with global->LDS copies of 1 KB each: every copy covers whole
-// 128-byte lines, where a load straight into B-operand registers covers 16
-// rows x 64 bytes (half a line per row), and the key path holds no
-// registers.  A slot stores row r's
-// 16-byte piece p at piece p ^ (r mod pieces-per-row), so the B-operand reads
-// of 16 rows at one piece hit distinct banks.  The loop body is free of
+// chunk.  A chunk is 16 consecutive key rows, one contiguous run of 16 x ROWB
+// bytes, and each wave moves its chunks into a ring of R LDS slots of its
+// own with global->LDS copies of 1 KB each: every copy covers whole 128-byte
+// lines, where a load straight into B-operand registers covers 16 rows x 64
+// bytes (half a line per row), and the key path holds no registers.  A slot
+// is refilled as soon as its chunk is in registers, so with two slots two
+// chunks are in flight during each chunk's contraction.  A slot stores row
+// r's 16-byte piece p at piece p ^ (r mod pieces-per-row), so the B-operand
+// reads of 16 rows at one piece hit distinct banks.  The loop body is free of
 // conditional memory operations: copies are always issued (rows past the
 // range are clamped to its last valid row and their scores ignored), and
-// scores go to a per-wave LDS buffer.  The scores (times the fp8 scale)
-// leave with coalesced stores after the loop.
-// LDS slots per wave.  A slot is refilled as soon as its chunk is in registers, so two
-// chunks are in flight during each chunk's contraction.
+// scores go to a per-wave LDS buffer.  The scores (times the fp8 scale) leave
+// with coalesced stores after the loop.
 constexpr int kDecRing = 2;
 constexpr int kDecBuf = kDecMaxSpan + 16 * kDecRing;  // + the ring's overrun
 
