@@ -82,6 +82,15 @@ def test_fullsize_decode_32k():
     _decode_full(wl, seqs=[0, 13, 31], attn_atol=ATTN_ATOL_BF16)
 
 
+def test_decode_64_sequences_1024_positions_per_wave():
+    # 64 rows of 32768 positions fill the score kernel's 512 work-groups at
+    # its longest span, 1024 positions (64 chunks) per wave, and a candidate
+    # list of 4096 slots per work-group; the batch above runs 512 per wave
+    _announce("decode B=64 L=32768 k=2048 bf16 (1024 positions per wave)")
+    wl = workloads.decode_32k(B=64)
+    _decode_full(wl, seqs=[0, 37, 63], attn_atol=ATTN_ATOL_BF16)
+
+
 def test_fullsize_decode_128k_fp8():
     _announce("decode B=8 L=131072 k=2048 fp8 keys")
     wl = workloads.decode_128k_fp8()
